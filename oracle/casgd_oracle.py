@@ -1,0 +1,318 @@
+"""FP64 CPU oracle for mixed-precision communication-avoiding SGD (CA-SGD) on
+generalized linear models.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the test-suite, the package smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP library
+and imports nothing from the package; the two meet only through the seeded
+input generators, which hold none of the method's arithmetic.
+
+Source of the method: "Mixed-Precision Communication-Avoiding SGD for
+Generalized Linear Models on GPUs" (paperdance.org/p/2606.18463), Abstract.
+The abstract names the pieces (an outer iteration of s minibatch steps whose
+s AllReduces become one AllReduce of an sb x sb Gram matrix; data stored in
+low precision; the Gram built from low-precision inputs with high-precision
+accumulation; inner recurrence and weight update in high precision) but prints
+no formula.  The algebra below is the plain minibatch-SGD step unrolled over s
+minibatches, which is what replacing s AllReduces by one Gram requires:
+
+    SGD on minibatch j:   w_j = w_{j-1} - (eta/b) * Y_j^T r_j,
+                          r_j = l'(Y_j w_{j-1}, y_j)
+    unrolled:             Y_j w_{j-1} = Y_j w_0 - (eta/b) * sum_{t<j} (Y_j Y_t^T) r_t
+    so with v = Y w_0 and G_{j,t} = Y_j Y_t^T:
+                          z_j = v_j - (eta/b) * sum_{t<j} G_{j,t} r_t,  r_j = l'(z_j, y_j)
+                          w_s = w_0 - (eta/b) * Y^T [r_1; ...; r_s]
+
+Readings taken where the page is silent (each is listed in the design notes):
+  * sampling: i.i.d. uniform with replacement; index i of an outer step with
+    seed S is floor(x_i * m / 2^64) where x_i is output i of the SplitMix64
+    stream seeded with S (Steele, Lea & Flood, OOPSLA 2014; multiply-high range
+    reduction as in Lemire, ACM TOMS 2019).  The seed of outer step k is output
+    k of the SplitMix64 stream seeded with the run's base seed.
+  * the step is eta/b times the minibatch SUM of per-row derivatives.
+  * "linear" regression uses the squared loss l = (z - y)^2 / 2.
+  * no regularisation.
+  * low precision = bfloat16 with round-to-nearest, ties to even.
+  * eta enters as the float32 value the GPU receives, widened to float64.
+
+Parity status of each function:
+  splitmix64, sample_indices ...... pinned (published known-answer values,
+                                     big-integer range reduction, chi-square)
+  bf16_bits / stored_values ....... pinned (torch CPU conversion, built ties)
+  loss_terms / loss_derivative .... pinned (finite differences, closed forms)
+  gram_blocks ..................... pinned (brute-force triple loop)
+  outer_step ...................... pinned (equals s plain SGD steps; s = 1;
+                                     squared loss = linear solve; exact
+                                     rational arithmetic; orthogonal rows)
+  full_loss / full_gradient ....... pinned (closed forms at w = 0; finite
+                                     differences)
+  train (many outer steps) ........ parity unpinned beyond the per-step pins
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+MASK64 = (1 << 64) - 1
+# SplitMix64 constants, as published with the generator (Steele, Lea & Flood 2014).
+SPLITMIX_GAMMA = 0x9E3779B97F4A7C15
+SPLITMIX_M1 = 0xBF58476D1CE4E5B9
+SPLITMIX_M2 = 0x94D049BB133111EB
+
+LOSSES = ("logistic", "squared", "poisson")
+
+
+# --------------------------------------------------------------------------
+# sampling
+# --------------------------------------------------------------------------
+def splitmix64(seed: int, i: int) -> int:
+    """Output number i (0-based) of the SplitMix64 stream seeded with `seed`.
+
+    The generator's state advances by the golden-ratio increment before each
+    output, so output i mixes seed + (i + 1) * gamma.  Pure Python integers.
+    """
+    z = (int(seed) + (int(i) + 1) * SPLITMIX_GAMMA) & MASK64
+    z = ((z ^ (z >> 30)) * SPLITMIX_M1) & MASK64
+    z = ((z ^ (z >> 27)) * SPLITMIX_M2) & MASK64
+    return z ^ (z >> 31)
+
+
+def step_seed(base_seed: int, k: int) -> int:
+    """Seed of outer step k: output k of the stream seeded with the base seed."""
+    return splitmix64(base_seed, k)
+
+
+def sample_indices(seed: int, m: int, count: int) -> np.ndarray:
+    """Row indices of one outer step: floor(x_i * m / 2^64), i < count.
+
+    Sampling with replacement (a reading: the page does not say how
+    minibatches are drawn).  Minibatch j is entries [j*b, (j+1)*b).
+    """
+    out = np.empty(count, dtype=np.int64)
+    for i in range(count):
+        out[i] = (splitmix64(seed, i) * int(m)) >> 64
+    return out
+
+
+# --------------------------------------------------------------------------
+# low-precision storage
+# --------------------------------------------------------------------------
+def bf16_bits(x) -> np.ndarray:
+    """bfloat16 bit patterns of float32 values, round-to-nearest ties-to-even.
+
+    Integer formulation: add 0x7FFF plus the lowest kept bit, then drop the
+    16 low bits.  NaNs keep their sign and become quiet NaNs.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    is_nan = (u & 0x7FFFFFFF) > 0x7F800000
+    lsb = (u >> 16) & 1
+    rounded = ((u + 0x7FFF + lsb) >> 16) & 0xFFFF
+    quiet = ((u >> 16) | 0x0040) & 0xFFFF
+    return np.where(is_nan, quiet, rounded).astype(np.uint16)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact float64 value of bfloat16 bit patterns."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def stored_values(x_f32, storage: str) -> np.ndarray:
+    """The values the method stores for float32 data, as float64."""
+    if storage == "bf16":
+        return bf16_to_f64(bf16_bits(x_f32))
+    if storage == "fp32":
+        return np.asarray(x_f32, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown storage {storage!r}")
+
+
+# --------------------------------------------------------------------------
+# per-row losses of the three generalized linear models
+# --------------------------------------------------------------------------
+def _softplus(u):
+    return np.maximum(u, 0.0) + np.log1p(np.exp(-np.abs(u)))
+
+
+def _sigmoid(u):
+    out = np.empty_like(u)
+    pos = u >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-u[pos]))
+    e = np.exp(u[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def loss_terms(z, y, loss: str) -> np.ndarray:
+    """Per-row loss l(z, y).
+
+    logistic (y = +-1):  log(1 + exp(-y z))
+    squared:             (z - y)^2 / 2
+    poisson (counts y):  exp(z) - y z
+    """
+    z = np.asarray(z, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    if loss == "logistic":
+        return _softplus(-y * z)
+    if loss == "squared":
+        return 0.5 * (z - y) ** 2
+    if loss == "poisson":
+        return np.exp(z) - y * z
+    raise ValueError(f"unknown loss {loss!r}")
+
+
+def loss_derivative(z, y, loss: str) -> np.ndarray:
+    """d l(z, y) / dz.
+
+    logistic:  -y * sigmoid(-y z)
+    squared:   z - y
+    poisson:   exp(z) - y
+    """
+    z = np.atleast_1d(np.asarray(z, dtype=np.float64))
+    y = np.atleast_1d(np.asarray(y, dtype=np.float64))
+    if loss == "logistic":
+        return -y * _sigmoid(-y * z)
+    if loss == "squared":
+        return z - y
+    if loss == "poisson":
+        return np.exp(z) - y
+    raise ValueError(f"unknown loss {loss!r}")
+
+
+# --------------------------------------------------------------------------
+# one outer iteration
+# --------------------------------------------------------------------------
+def step_size(eta, b: int) -> float:
+    """eta / b with eta taken as the float32 value handed to the GPU."""
+    return float(np.float64(np.float32(eta))) / float(b)
+
+
+def gather(X_f32, y_f32, idx, storage: str):
+    """Y = stored rows X[idx] and y_B = y[idx], both float64.
+
+    Rounding is elementwise, so rounding the gathered rows equals gathering
+    rounded rows; this keeps the oracle's memory at the sample's size.
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    Y = stored_values(np.asarray(X_f32)[idx], storage)
+    yB = np.asarray(y_f32, dtype=np.float32)[idx].astype(np.float64)
+    return Y, yB
+
+
+def gram_blocks(Y, s: int, b: int) -> dict:
+    """G_{j,t} = Y_j Y_t^T for 0 <= t < j < s (0-based minibatch numbers).
+
+    Only the strictly-lower block triangle: the recurrence never reads the
+    diagonal blocks or the upper triangle.  With bfloat16 inputs every product
+    is exact in float64, so the blocks are the exact Gram up to float64 sums.
+    """
+    G = {}
+    for j in range(s):
+        Yj = Y[j * b:(j + 1) * b]
+        for t in range(j):
+            G[(j, t)] = Yj @ Y[t * b:(t + 1) * b].T
+    return G
+
+
+def recurrence(G: dict, v, yB, s: int, b: int, eta, loss: str):
+    """Inner recurrence: z_j = v_j - (eta/b) sum_{t<j} G_{j,t} r_t, r_j = l'(z_j, y_j)."""
+    c = step_size(eta, b)
+    z = np.empty(s * b)
+    r = np.empty(s * b)
+    for j in range(s):
+        acc = np.zeros(b)
+        for t in range(j):
+            acc += G[(j, t)] @ r[t * b:(t + 1) * b]
+        z[j * b:(j + 1) * b] = v[j * b:(j + 1) * b] - c * acc
+        r[j * b:(j + 1) * b] = loss_derivative(z[j * b:(j + 1) * b], yB[j * b:(j + 1) * b], loss)
+    return z, r
+
+
+def outer_step_rows(Y, yB, w0, s: int, b: int, eta, loss: str) -> dict:
+    """One CA-SGD outer iteration on already-gathered rows Y (s*b x n)."""
+    w0 = np.asarray(w0, dtype=np.float64)
+    c = step_size(eta, b)
+    G = gram_blocks(Y, s, b)
+    v = Y @ w0
+    z, r = recurrence(G, v, yB, s, b, eta, loss)
+    w = w0 - c * (Y.T @ r)
+    return {"G": G, "v": v, "z": z, "r": r, "w": w}
+
+
+def outer_step(X_f32, y_f32, w0, s: int, b: int, eta, seed: int, loss: str,
+               storage: str = "bf16", idx=None) -> dict:
+    """One outer step from the full data: sample (or take idx), gather, step."""
+    m = np.asarray(X_f32).shape[0]
+    if idx is None:
+        idx = sample_indices(seed, m, s * b)
+    Y, yB = gather(X_f32, y_f32, idx, storage)
+    out = outer_step_rows(Y, yB, w0, s, b, eta, loss)
+    out["idx"] = np.asarray(idx, dtype=np.int64)
+    out["Y"] = Y
+    out["yB"] = yB
+    return out
+
+
+# --------------------------------------------------------------------------
+# plain minibatch SGD (what CA-SGD reorganises)
+# --------------------------------------------------------------------------
+def sgd_steps(Y, yB, w0, s: int, b: int, eta, loss: str) -> np.ndarray:
+    """s plain minibatch SGD steps on the minibatches of Y, in order."""
+    c = step_size(eta, b)
+    w = np.array(w0, dtype=np.float64)
+    for j in range(s):
+        Yj = Y[j * b:(j + 1) * b]
+        w = w - c * (Yj.T @ loss_derivative(Yj @ w, yB[j * b:(j + 1) * b], loss))
+    return w
+
+
+# --------------------------------------------------------------------------
+# loss over the whole data set, and multi-step runs
+# --------------------------------------------------------------------------
+def full_loss(X_f32, y_f32, w, loss: str, storage: str = "bf16",
+              chunk: int = 1 << 16) -> float:
+    """f(w) = (1/m) sum_i l(x_i . w, y_i) over every row, in float64."""
+    X_f32 = np.asarray(X_f32)
+    m = X_f32.shape[0]
+    w = np.asarray(w, dtype=np.float64)
+    total = 0.0
+    for a in range(0, m, chunk):
+        Xc = stored_values(X_f32[a:a + chunk], storage)
+        total += float(np.sum(loss_terms(Xc @ w, np.asarray(y_f32[a:a + chunk], np.float64), loss)))
+    return total / m
+
+
+def full_gradient(X_f32, y_f32, w, loss: str, storage: str = "bf16") -> np.ndarray:
+    """grad f(w) = (1/m) X^T l'(X w, y) over every row."""
+    X = stored_values(X_f32, storage)
+    y = np.asarray(y_f32, dtype=np.float64)
+    return X.T @ loss_derivative(X @ np.asarray(w, np.float64), y, loss) / X.shape[0]
+
+
+def train(X_f32, y_f32, w0, s: int, b: int, eta, loss: str, base_seed: int,
+          n_outer: int, storage: str = "bf16", first_step: int = 0,
+          method: str = "ca") -> np.ndarray:
+    """n_outer outer steps from w0; step k samples with step_seed(base_seed, k).
+
+    method "ca" runs the CA-SGD outer iteration, "sgd" runs s plain SGD steps
+    on the same minibatches.
+    """
+    m = np.asarray(X_f32).shape[0]
+    w = np.array(w0, dtype=np.float64)
+    for k in range(first_step, first_step + n_outer):
+        idx = sample_indices(step_seed(base_seed, k), m, s * b)
+        Y, yB = gather(X_f32, y_f32, idx, storage)
+        if method == "ca":
+            w = outer_step_rows(Y, yB, w, s, b, eta, loss)["w"]
+        elif method == "sgd":
+            w = sgd_steps(Y, yB, w, s, b, eta, loss)
+        else:
+            raise ValueError(method)
+    return w
+
+
+def gram_bytes(s: int, b: int, packed: bool) -> int:
+    """Bytes of the float32 Gram an AllReduce would carry: full sb x sb, or the
+    strictly-lower block triangle only (s(s-1)/2 blocks of b x b)."""
+    if packed:
+        return 4 * b * b * s * (s - 1) // 2
+    return 4 * (s * b) ** 2

@@ -1,0 +1,362 @@
+"""Pins of the CPU oracle to facts it does not compute itself.
+
+Each test checks the oracle against something independent of its own code:
+published known-answer values, a library routine, a closed form, brute force,
+exact rational arithmetic, or the identity that defines the method (CA-SGD is
+s plain minibatch SGD steps reorganised around the Gram matrix; Abstract of
+"Mixed-Precision Communication-Avoiding SGD for Generalized Linear Models on
+GPUs").  The last test plants plausible mistakes in a copy of the oracle's
+recurrence and checks that the pins catch every one.
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import casgd_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LOSSES = ("logistic", "squared", "poisson")
+
+
+def _read_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def _targets(rng, k, loss):
+    if loss == "logistic":
+        return np.where(rng.random(k) < 0.5, -1.0, 1.0)
+    if loss == "squared":
+        return rng.standard_normal(k)
+    return rng.poisson(1.5, k).astype(np.float64)
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+# ---------------------------------------------------------------- sampler
+def test_splitmix64_known_answers():
+    rows = _read_rows("splitmix64_kat.txt")
+    assert len(rows) >= 6
+    for seed, i, out in rows:
+        assert O.splitmix64(int(seed), int(i)) == int(out)
+
+
+def test_step_seed_is_stream_output():
+    # outer step k's seed is output k of the base stream (known answers above)
+    assert O.step_seed(0, 0) == 16294208416658607535
+    assert O.step_seed(0, 2) == 487617019471545679
+
+
+def test_sample_power_of_two_takes_top_bits():
+    # for m = 2^k the multiply-high range reduction keeps the top k bits
+    for k in (1, 7, 20, 31):
+        idx = O.sample_indices(12345, 1 << k, 64)
+        top = [O.splitmix64(12345, i) >> (64 - k) for i in range(64)]
+        assert idx.tolist() == top
+
+
+def test_sample_matches_exact_division():
+    m = 400_000
+    idx = O.sample_indices(99, m, 256)
+    for i in range(256):
+        x = O.splitmix64(99, i)
+        assert idx[i] == math.floor(Fraction(x * m, 1 << 64))
+    assert idx.min() >= 0 and idx.max() < m
+
+
+def test_sample_uniform_chi_square():
+    from scipy.stats import chisquare
+    m = 1000
+    idx = O.sample_indices(7, m, 200_000)
+    counts = np.bincount(idx, minlength=m)
+    assert chisquare(counts).pvalue > 1e-4
+
+
+# ---------------------------------------------------------------- bf16
+def test_bf16_hand_built_cases():
+    for f32, bf, *_ in _read_rows("bf16_rne_cases.txt"):
+        x = np.array([int(f32, 16)], dtype=np.uint32).view(np.float32)
+        assert int(O.bf16_bits(x)[0]) == int(bf, 16), f32
+
+
+def test_bf16_matches_torch_cpu_conversion():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),
+        rng.integers(0, 1 << 32, 20000, dtype=np.uint64).astype(np.uint32).view(np.float32),
+    ])
+    x = x[~np.isnan(x)]  # torch canonicalises NaN payloads; NaNs are covered above
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_bits(x), ref)
+
+
+def test_bf16_values_exact_and_close():
+    x = np.linspace(-3, 3, 1001).astype(np.float32)
+    v = O.stored_values(x, "bf16")
+    assert np.all(np.abs(v - x) <= np.abs(x) * 2.0 ** -8 + 1e-45)
+    assert np.array_equal(O.stored_values(x, "fp32"), x.astype(np.float64))
+
+
+# ---------------------------------------------------------------- losses
+@pytest.mark.parametrize("loss", LOSSES)
+def test_derivative_matches_finite_differences(loss):
+    rng = np.random.default_rng(11)
+    z = rng.uniform(-3, 3, 64)
+    y = _targets(rng, 64, loss)
+    h = 1e-6
+    fd = (O.loss_terms(z + h, y, loss) - O.loss_terms(z - h, y, loss)) / (2 * h)
+    d = O.loss_derivative(z, y, loss)
+    assert np.max(np.abs(fd - d) / (1 + np.abs(d))) < 1e-7
+
+
+def test_closed_forms_at_zero():
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((50, 4)).astype(np.float32)
+    w = np.zeros(4)
+    ylog = np.where(rng.random(50) < 0.5, -1.0, 1.0).astype(np.float32)
+    ysq = rng.standard_normal(50).astype(np.float32)
+    ypo = rng.poisson(2.0, 50).astype(np.float32)
+    assert abs(O.full_loss(X, ylog, w, "logistic") - math.log(2.0)) < 1e-15
+    assert abs(O.full_loss(X, ysq, w, "squared") - 0.5 * np.mean(ysq.astype(np.float64) ** 2)) < 1e-15
+    assert abs(O.full_loss(X, ypo, w, "poisson") - 1.0) < 1e-15
+    z0 = np.zeros(50)
+    assert np.array_equal(O.loss_derivative(z0, ylog, "logistic"), -ylog / 2.0)
+    assert np.array_equal(O.loss_derivative(z0, ysq, "squared"), -ysq.astype(np.float64))
+    assert np.array_equal(O.loss_derivative(z0, ypo, "poisson"), 1.0 - ypo)
+
+
+def test_logistic_is_stable_at_large_margins():
+    z = np.array([-800.0, -40.0, 40.0, 800.0])
+    y = np.ones(4)
+    lt = O.loss_terms(z, y, "logistic")
+    assert np.all(np.isfinite(lt))
+    assert abs(lt[0] - 800.0) < 1e-12 and lt[3] < 1e-300
+    d = O.loss_derivative(z, y, "logistic")
+    assert np.all(np.isfinite(d)) and abs(d[0] + 1.0) < 1e-15 and abs(d[3]) < 1e-300
+
+
+# ---------------------------------------------------------------- Gram
+def test_gram_blocks_brute_force():
+    rng = np.random.default_rng(2)
+    s, b, n = 4, 3, 5
+    Y = rng.standard_normal((s * b, n))
+    G = O.gram_blocks(Y, s, b)
+    assert sorted(G) == [(j, t) for j in range(s) for t in range(j)]
+    for (j, t), blk in G.items():
+        for i in range(b):
+            for k in range(b):
+                ref = sum(Y[j * b + i, c] * Y[t * b + k, c] for c in range(n))
+                assert abs(blk[i, k] - ref) < 1e-12
+
+
+# ---------------------------------------------------------------- outer step
+@pytest.mark.parametrize("loss", LOSSES)
+@pytest.mark.parametrize("s,b", [(1, 4), (2, 3), (4, 8), (7, 1), (5, 16)])
+def test_ca_step_equals_s_sgd_steps(loss, s, b):
+    rng = np.random.default_rng(100 * s + b)
+    n = 9
+    Y = O.stored_values(rng.standard_normal((s * b, n)).astype(np.float32) * 0.4, "bf16")
+    yB = _targets(rng, s * b, loss)
+    w0 = rng.standard_normal(n) * 0.5
+    ca = O.outer_step_rows(Y, yB, w0, s, b, 0.7, loss)["w"]
+    sgd = O.sgd_steps(Y, yB, w0, s, b, 0.7, loss)
+    assert _rel(ca, sgd) <= 1e-10
+
+
+@pytest.mark.parametrize("loss", LOSSES)
+def test_s1_reduces_to_one_sgd_step(loss):
+    rng = np.random.default_rng(17)
+    b, n = 6, 5
+    Y = rng.standard_normal((b, n))
+    yB = _targets(rng, b, loss)
+    w0 = rng.standard_normal(n)
+    out = O.outer_step_rows(Y, yB, w0, 1, b, 0.3, loss)
+    assert out["G"] == {}
+    assert np.array_equal(out["z"], Y @ w0)
+    c = float(np.float32(0.3)) / b
+    g = O.loss_derivative(Y @ w0, yB, loss)
+    manual = w0 - c * np.array([sum(Y[i, k] * g[i] for i in range(b)) for k in range(n)])
+    assert _rel(out["w"], manual) <= 1e-13
+
+
+def test_squared_recurrence_is_a_block_triangular_solve():
+    rng = np.random.default_rng(23)
+    s, b, n = 6, 4, 7
+    Y = rng.standard_normal((s * b, n))
+    yB = rng.standard_normal(s * b)
+    w0 = rng.standard_normal(n)
+    eta = 0.25
+    out = O.outer_step_rows(Y, yB, w0, s, b, eta, "squared")
+    c = float(np.float32(eta)) / b
+    full = Y @ Y.T
+    L = np.zeros_like(full)
+    for j in range(s):
+        L[j * b:(j + 1) * b, :j * b] = full[j * b:(j + 1) * b, :j * b]
+    v = Y @ w0
+    z = np.linalg.solve(np.eye(s * b) + c * L, v + c * L @ yB)
+    assert _rel(out["z"], z) <= 1e-12
+
+
+def test_squared_step_matches_exact_rationals():
+    # dyadic inputs are exact in float64; plain SGD in Fractions is the exact answer
+    rng = np.random.default_rng(29)
+    s, b, n = 3, 2, 3
+    Yi = rng.integers(-8, 9, (s * b, n))
+    yi = rng.integers(-8, 9, s * b)
+    wi = rng.integers(-8, 9, n)
+    Y = Yi / 8.0
+    yB = yi / 4.0
+    w0 = wi / 16.0
+    eta = 0.375  # exact in float32
+    c = Fraction(3, 8) / b
+    w = [Fraction(int(v), 16) for v in wi]
+    for j in range(s):
+        rows = range(j * b, (j + 1) * b)
+        g = [sum(Fraction(int(Yi[i, k]), 8) * w[k] for k in range(n)) - Fraction(int(yi[i]), 4) for i in rows]
+        w = [w[k] - c * sum(Fraction(int(Yi[i, k]), 8) * g[ii] for ii, i in enumerate(rows)) for k in range(n)]
+    exact = np.array([float(x) for x in w])
+    got = O.outer_step_rows(Y, yB, w0, s, b, eta, "squared")["w"]
+    assert _rel(got, exact) <= 1e-14
+
+
+@pytest.mark.parametrize("loss", LOSSES)
+def test_orthogonal_rows_decouple(loss):
+    n = 12
+    X = np.eye(n, dtype=np.float32)
+    rng = np.random.default_rng(31)
+    y = _targets(rng, n, loss).astype(np.float32)
+    idx = rng.permutation(n)[:8]
+    w0 = (rng.standard_normal(n) * 0.5).astype(np.float32).astype(np.float64)
+    out = O.outer_step(X, y, w0, 4, 2, 0.5, 0, loss, storage="fp32", idx=idx)
+    for blk in out["G"].values():
+        assert not np.any(blk)
+    c = float(np.float32(0.5)) / 2
+    expect = w0.copy()
+    for i in idx:
+        expect[i] -= c * O.loss_derivative(w0[i], y[i], loss)[0]
+    assert _rel(out["w"], expect) <= 1e-15
+
+
+@pytest.mark.parametrize("loss", LOSSES)
+def test_full_gradient_matches_finite_differences(loss):
+    rng = np.random.default_rng(37)
+    m, n = 8, 3
+    X = (rng.standard_normal((m, n)) * 0.5).astype(np.float32)
+    y = _targets(rng, m, loss).astype(np.float32)
+    w = rng.standard_normal(n) * 0.3
+    g = O.full_gradient(X, y, w, loss)
+    h = 1e-6
+    for k in range(n):
+        e = np.zeros(n)
+        e[k] = h
+        fd = (O.full_loss(X, y, w + e, loss) - O.full_loss(X, y, w - e, loss)) / (2 * h)
+        assert abs(fd - g[k]) <= 1e-7 * (1 + abs(g[k]))
+
+
+@pytest.mark.parametrize("loss", LOSSES)
+def test_training_run_ca_equals_sgd(loss):
+    rng = np.random.default_rng(41)
+    m, n = 300, 6
+    X = (rng.standard_normal((m, n)) * 0.4).astype(np.float32)
+    y = _targets(rng, m, loss).astype(np.float32)
+    w0 = np.zeros(n)
+    a = O.train(X, y, w0, 4, 8, 0.2, loss, base_seed=5, n_outer=10, method="ca")
+    b = O.train(X, y, w0, 4, 8, 0.2, loss, base_seed=5, n_outer=10, method="sgd")
+    assert _rel(a, b) <= 1e-10
+    # resuming after 4 steps reproduces the indices exactly
+    w4 = O.train(X, y, w0, 4, 8, 0.2, loss, base_seed=5, n_outer=4)
+    w10 = O.train(X, y, w4, 4, 8, 0.2, loss, base_seed=5, n_outer=6, first_step=4)
+    assert np.array_equal(w10, a)
+
+
+def test_gram_bytes():
+    assert O.gram_bytes(16, 64, packed=False) == 4 * 1024 * 1024
+    assert O.gram_bytes(16, 64, packed=True) == 120 * 64 * 64 * 4
+    assert O.gram_bytes(1, 64, packed=True) == 0
+
+
+# ---------------------------------------------------------------- pin sensitivity
+def _broken_recurrences():
+    def drop_last(G, v, yB, s, b, eta, loss):
+        c = O.step_size(eta, b)
+        z = np.empty(s * b)
+        r = np.empty(s * b)
+        for j in range(s):
+            acc = np.zeros(b)
+            for t in range(j - 1):  # the t = j-1 term dropped
+                acc += G[(j, t)] @ r[t * b:(t + 1) * b]
+            z[j * b:(j + 1) * b] = v[j * b:(j + 1) * b] - c * acc
+            r[j * b:(j + 1) * b] = O.loss_derivative(z[j * b:(j + 1) * b], yB[j * b:(j + 1) * b], loss)
+        return z, r
+
+    def wrong_sign(G, v, yB, s, b, eta, loss):
+        c = O.step_size(eta, b)
+        z = np.empty(s * b)
+        r = np.empty(s * b)
+        for j in range(s):
+            acc = np.zeros(b)
+            for t in range(j):
+                acc += G[(j, t)] @ r[t * b:(t + 1) * b]
+            z[j * b:(j + 1) * b] = v[j * b:(j + 1) * b] + c * acc
+            r[j * b:(j + 1) * b] = O.loss_derivative(z[j * b:(j + 1) * b], yB[j * b:(j + 1) * b], loss)
+        return z, r
+
+    def transposed_block(G, v, yB, s, b, eta, loss):
+        c = O.step_size(eta, b)
+        z = np.empty(s * b)
+        r = np.empty(s * b)
+        for j in range(s):
+            acc = np.zeros(b)
+            for t in range(j):
+                acc += G[(j, t)].T @ r[t * b:(t + 1) * b]
+            z[j * b:(j + 1) * b] = v[j * b:(j + 1) * b] - c * acc
+            r[j * b:(j + 1) * b] = O.loss_derivative(z[j * b:(j + 1) * b], yB[j * b:(j + 1) * b], loss)
+        return z, r
+
+    def wrong_index(G, v, yB, s, b, eta, loss):
+        c = O.step_size(eta, b)
+        z = np.empty(s * b)
+        r = np.empty(s * b)
+        for j in range(s):
+            acc = np.zeros(b)
+            for t in range(j):
+                acc += G[(j, t)] @ r[t * b:(t + 1) * b]
+            z[j * b:(j + 1) * b] = v[j * b:(j + 1) * b] - c * acc
+            # derivative taken against the previous minibatch's targets
+            yy = yB[max(j - 1, 0) * b:max(j - 1, 0) * b + b]
+            r[j * b:(j + 1) * b] = O.loss_derivative(z[j * b:(j + 1) * b], yy, loss)
+        return z, r
+
+    return [drop_last, wrong_sign, transposed_block, wrong_index]
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    rng = np.random.default_rng(43)
+    s, b, n = 4, 3, 5
+    Y = rng.standard_normal((s * b, n)) * 0.5
+    yB = np.where(rng.random(s * b) < 0.5, -1.0, 1.0)
+    w0 = rng.standard_normal(n)
+    sgd = O.sgd_steps(Y, yB, w0, s, b, 0.7, "logistic")
+    good = O.outer_step_rows(Y, yB, w0, s, b, 0.7, "logistic")["w"]
+    assert _rel(good, sgd) <= 1e-10
+    for broken in _broken_recurrences():
+        monkeypatch.setattr(O, "recurrence", broken)
+        bad = O.outer_step_rows(Y, yB, w0, s, b, 0.7, "logistic")["w"]
+        assert _rel(bad, sgd) > 1e-6, broken.__name__
+        monkeypatch.undo()
