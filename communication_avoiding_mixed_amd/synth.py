@@ -58,7 +58,7 @@ WORKLOADS = {
     "poisson-synth": Workload("poisson-synth", 2_000_000, 256, 16, 128, 0.01, "poisson", 200),
 }
 
-_CHUNK = 1 << 16
+_CHUNK = 1 << 13
 
 
 def _matvec64(X, w):

@@ -268,11 +268,11 @@ def sgd_steps(Y, yB, w0, s: int, b: int, eta, loss: str) -> np.ndarray:
 # --------------------------------------------------------------------------
 # loss over the whole data set, and multi-step runs
 # --------------------------------------------------------------------------
-def full_loss(X_f32, y_f32, w, loss: str, storage: str = "bf16",
-              chunk: int = 1 << 16) -> float:
+def full_loss(X_f32, y_f32, w, loss: str, storage: str = "bf16") -> float:
     """f(w) = (1/m) sum_i l(x_i . w, y_i) over every row, in float64."""
     X_f32 = np.asarray(X_f32)
     m = X_f32.shape[0]
+    chunk = max(1, (1 << 21) // max(1, X_f32.shape[1]))
     w = np.asarray(w, dtype=np.float64)
     total = 0.0
     for a in range(0, m, chunk):
