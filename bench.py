@@ -1,0 +1,187 @@
+"""Throughput of mixed-precision CA-SGD outer iterations on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload epsilon]
+
+A step is one outer iteration (s inner SGD steps): sample + gather + margins,
+strictly-lower Gram on bf16 MFMA, inner recurrence, weight update.  The data
+(seeded, synthetic, epsilon-shaped by default) is resident in HBM before the
+timed region.  Prints one JSON line with the whole-step throughput (inner SGD
+steps/s), the Gram kernel's roofline figures measured with HIP events on the
+library's stream, and the CPU oracle timed on the host on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+METRIC = "inner SGD steps/s and Gram TFLOP/s (% of roofline) at epsilon-shape, 1 GPU"
+
+
+def algorithmic(wl):
+    """Algorithmic work of one outer step (no padding, no staging copies)."""
+    s, b, n = wl.s, wl.b, wl.n
+    sb = s * b
+    gram_flops = n * b * b * s * (s - 1)          # strictly-lower blocks only
+    g_bytes = 2 * b * b * s * (s - 1)              # packed float32 G
+    return {
+        "gram_flops": gram_flops,
+        "gather_bytes": sb * n * 2 + sb * 12 + n * 4,   # rows read, idx/yB/v, w
+        "gram_bytes": sb * n * 2 + g_bytes,             # Y read, G written
+        "recur_bytes": g_bytes + sb * 16,               # G read, v/yB in, z/r out
+        "update_bytes": sb * n * 2 + sb * 4 + 2 * n * 4,  # Y read, r, w read+write
+        "B_A": sb * n * 2 + g_bytes,
+        "B_B": g_bytes,
+        "B_C": sb * n * 2 + 2 * n * 4,
+    }
+
+
+def cpu_baseline(X, y, wl, budget_s: float):
+    """The oracle's outer step, as it stands, on the host: inner steps/s."""
+    import numpy as np
+    from oracle import casgd_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    w = np.zeros(wl.n)
+    t0 = time.perf_counter()
+    k = 0
+    while True:
+        w = O.outer_step(X, y, w, wl.s, wl.b, wl.eta, O.step_seed(0, k), wl.loss)["w"]
+        k += 1
+        el = time.perf_counter() - t0
+        if (el >= budget_s and k >= 2) or k >= wl.outer:
+            break
+    return {
+        "value": wl.s * k / el,
+        "unit": "inner SGD steps/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {k} outer steps (s={wl.s}, b={wl.b}) of the same {wl.name} run from w=0, "
+                  f"float64 NumPy, {el:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="epsilon")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU "
+              "column-partitioned path is not built", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from communication_avoiding_mixed_amd import binding as B
+    from communication_avoiding_mixed_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    X, y = synth.make_data(wl.name)
+    print(f"[bench] data {wl.name} {X.shape} ready in {time.time() - t0:.0f}s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    h = B.CASGD(torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev), wl.loss, wl.storage)
+    stream = torch.cuda.Stream()
+    w = torch.zeros(wl.n, device=dev)
+    with torch.cuda.stream(stream):
+        # warm-up
+        h.train(wl.s, wl.b, wl.eta, 0, 0, args.warmup, w)
+        stream.synchronize()
+        # timed region: exactly K outer steps
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        h.train(wl.s, wl.b, wl.eta, 0, args.warmup, args.steps, w)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop)
+        # the same K steps again with per-kernel HIP events on the library's stream
+        h.set_timing(True)
+        w2 = torch.zeros(wl.n, device=dev)
+        h.train(wl.s, wl.b, wl.eta, 0, 0, args.steps, w2)
+        per = {}
+        for kid, kname in B.KERNEL_NAMES.items():
+            tot, cnt = h.timing(kid, reset=True)
+            per[kname] = (tot / max(cnt, 1)) * 1e3  # microseconds per launch
+        h.set_timing(False)
+        loss = h.loss_value(w)
+    ms_per_step = ms / args.steps
+    value = wl.s * args.steps / (ms / 1e3)
+
+    alg = algorithmic(wl)
+    gram_tflops = alg["gram_flops"] / (per["gram"] * 1e-6) / 1e12
+    kernels = {
+        "gather": {"us": per["gather"], "GB/s": alg["gather_bytes"] / (per["gather"] * 1e-6) / 1e9},
+        "gram": {"us": per["gram"], "TFLOP/s": gram_tflops,
+                 "GB/s": alg["gram_bytes"] / (per["gram"] * 1e-6) / 1e9},
+        "recur": {"us": per["recur"], "GB/s": alg["recur_bytes"] / (per["recur"] * 1e-6) / 1e9},
+        "update": {"us": per["update"], "GB/s": alg["update_bytes"] / (per["update"] * 1e-6) / 1e9},
+    }
+    for k in kernels.values():
+        for u in list(k):
+            if u == "TFLOP/s":
+                k["frac"] = k[u] / PEAK_BF16_TFLOPS
+            elif u == "GB/s" and "frac" not in k:
+                k["frac"] = k[u] / PEAK_HBM_GBS
+    t_roof = (max(alg["gram_flops"] / (PEAK_BF16_TFLOPS * 1e12), alg["B_A"] / (PEAK_HBM_GBS * 1e9))
+              + alg["B_B"] / (PEAK_HBM_GBS * 1e9) + alg["B_C"] / (PEAK_HBM_GBS * 1e9))
+    gram_bound_mfma = wl.n >= 512
+    if gram_bound_mfma:
+        roof = {"bound": "mfma", "achieved": gram_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": gram_tflops / PEAK_BF16_TFLOPS, "traffic": None}
+    else:
+        gbs = kernels["gram"]["GB/s"]
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+    roof["kernel"] = "gram_bf16_kernel"
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "inner SGD steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "m": wl.m, "n": wl.n, "s": wl.s, "b": wl.b, "eta": wl.eta,
+                   "loss": wl.loss, "storage": wl.storage, "accumulate": "f32",
+                   "gram_bytes_full": B.gram_bytes(wl.s, wl.b, packed=False),
+                   "gram_bytes_packed": B.gram_bytes(wl.s, wl.b, packed=True)},
+        "roofline": roof,
+        "step_roofline": {"t_roof_us": t_roof * 1e6, "t_meas_us": ms_per_step * 1e3,
+                          "frac": t_roof * 1e6 / (ms_per_step * 1e3)},
+        "kernels": kernels,
+        "final_loss": loss,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(X, y, wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,100 @@
+// Device-side helpers shared by the CA-SGD kernels: the counter-based row
+// sampler, bfloat16 storage conversion and the three GLM losses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace casgd {
+
+constexpr int kLogistic = 0;
+constexpr int kSquared = 1;
+constexpr int kPoisson = 2;
+
+// SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): output i of the stream
+// seeded with `seed` mixes seed + (i + 1) * golden-gamma.  Counter-based, so
+// every row index of an outer step is computed independently.
+__host__ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t i) {
+  uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Row i of an outer step: floor(x_i * m / 2^64), the multiply-high range
+// reduction (Lemire 2019).  Uniform with replacement over [0, m).
+__device__ __forceinline__ int32_t sample_row(uint64_t seed, uint64_t i, uint64_t m) {
+  return static_cast<int32_t>(__umul64hi(splitmix64(seed, i), m));
+}
+
+// float32 -> bfloat16 bits, round to nearest with ties to even; NaN -> quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Derivative of the per-row loss with respect to the margin z, in float32.
+//   logistic: -y * sigmoid(-y z) (exp of a non-positive argument only)
+//   squared:  z - y
+//   poisson:  exp(z) - y
+template <int LOSS>
+__device__ __forceinline__ float loss_deriv(float z, float y) {
+  if constexpr (LOSS == kLogistic) {
+    const float u = -y * z;
+    const float e = expf(-fabsf(u));
+    const float sig = u >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+    return -y * sig;
+  } else if constexpr (LOSS == kSquared) {
+    return z - y;
+  } else {
+    return expf(z) - y;
+  }
+}
+
+// Per-row loss in float64 from a float32 margin.
+//   logistic: softplus(-y z); squared: (z - y)^2 / 2; poisson: exp(z) - y z
+template <int LOSS>
+__device__ __forceinline__ double loss_value(double z, double y) {
+  if constexpr (LOSS == kLogistic) {
+    const double u = -y * z;
+    return fmax(u, 0.0) + log1p(exp(-fabs(u)));
+  } else if constexpr (LOSS == kSquared) {
+    const double d = z - y;
+    return 0.5 * d * d;
+  } else {
+    return exp(z) - y * z;
+  }
+}
+
+// Reduction over the `width` lanes of an aligned lane group (width a power of
+// two up to the 64-lane wavefront).
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, WIDTH);
+  return x;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ double group_sum_d(double x) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, WIDTH);
+  return x;
+}
+
+// Strictly-lower block (j, t), t < j, from its linear number p = j(j-1)/2 + t.
+__device__ __forceinline__ void block_of(int p, int& j, int& t) {
+  int jj = static_cast<int>((1.0f + sqrtf(1.0f + 8.0f * static_cast<float>(p))) * 0.5f);
+  while (jj * (jj - 1) / 2 > p) --jj;
+  while ((jj + 1) * jj / 2 <= p) ++jj;
+  j = jj;
+  t = p - jj * (jj - 1) / 2;
+}
+
+}  // namespace casgd

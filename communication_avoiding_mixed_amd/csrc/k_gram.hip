@@ -1,0 +1,224 @@
+// Strictly-lower block triangle of the Gram matrix G = Y Y^T.
+//
+// The Abstract of "Mixed-Precision Communication-Avoiding SGD for Generalized
+// Linear Models on GPUs" forms the sb x sb Gram from low-precision inputs with
+// high-precision accumulation on the GPU's matrix hardware; the inner
+// recurrence only ever reads blocks G_{j,t} with t < j, so only those are
+// computed.  On gfx950 this is bf16 MFMA (v_mfma_f32_32x32x16_bf16) with
+// float32 accumulators.  Both operands are rows of Y (an "NT" product), so
+// A and B tiles are staged through LDS the same way.
+//
+// Output layout (block-row): block-row j (1 <= j < s) is the b x (j*b)
+// row-major matrix [G_{j,0} ... G_{j,j-1}] starting at element b*b*j*(j-1)/2.
+#include "casgd_device.h"
+#include "casgd_internal.h"
+
+namespace casgd {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kTile = 64;  // output tile edge; 4 waves of 32 x 32
+
+// One 64 x 64 output tile per workgroup of 256 lanes.  blockIdx.x enumerates
+// (block (j,t), tile row, tile col); blockIdx.y is the problem (outer step).
+// Rows past the block edge (b not a multiple of 64) load as zeros and are not
+// stored.  K is walked in BK-wide stages, double-buffered through LDS.
+template <int BK>
+__global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restrict__ Y,
+                                                        int64_t ld, int s, int b, int tps,
+                                                        float* __restrict__ G, int64_t y_stride,
+                                                        int64_t g_stride) {
+  constexpr int CPR = BK / 8;          // 16-byte chunks per tile row per stage
+  constexpr int RPP = 256 / CPR;       // tile rows loaded per pass
+  constexpr int PASSES = kTile / RPP;  // passes per operand per stage
+  constexpr int LW = BK + 8;           // LDS row pitch (elements), breaks bank aliasing
+
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kTile * LW];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * LW];
+
+  const int nt2 = tps * tps;
+  const int p = blockIdx.x / nt2;
+  const int rem = blockIdx.x - p * nt2;
+  const int ti = rem / tps;
+  const int tj = rem - ti * tps;
+  int j, t;
+  block_of(p, j, t);
+  (void)s;
+
+  const uint16_t* Yp = Y + static_cast<int64_t>(blockIdx.y) * y_stride;
+  float* Gj = G + static_cast<int64_t>(blockIdx.y) * g_stride +
+              static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
+  const int64_t ldg = static_cast<int64_t>(j) * b;
+  const int a0 = ti * kTile;  // first row of the A tile inside block-row j
+  const int b0 = tj * kTile;  // first row of the B tile inside block-row t
+
+  const int lrow = threadIdx.x / CPR;
+  const int lchunk = threadIdx.x - lrow * CPR;
+  const uint16_t* aptr[PASSES];
+  const uint16_t* bptr[PASSES];
+  bool aok[PASSES], bok[PASSES];
+#pragma unroll
+  for (int q = 0; q < PASSES; ++q) {
+    const int r = lrow + q * RPP;
+    aok[q] = a0 + r < b;
+    bok[q] = b0 + r < b;
+    aptr[q] = Yp + (static_cast<int64_t>(j) * b + a0 + (aok[q] ? r : 0)) * ld + lchunk * 8;
+    bptr[q] = Yp + (static_cast<int64_t>(t) * b + b0 + (bok[q] ? r : 0)) * ld + lchunk * 8;
+  }
+
+  uint4 ra[PASSES], rb[PASSES];
+  auto load_stage = [&](int64_t k0) {
+    const bool kin = k0 + lchunk * 8 < ld;  // last stage may be half-width
+#pragma unroll
+    for (int q = 0; q < PASSES; ++q) {
+      ra[q] = (aok[q] && kin) ? *reinterpret_cast<const uint4*>(aptr[q] + k0) : make_uint4(0, 0, 0, 0);
+      rb[q] = (bok[q] && kin) ? *reinterpret_cast<const uint4*>(bptr[q] + k0) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < PASSES; ++q) {
+      const int r = lrow + q * RPP;
+      *reinterpret_cast<uint4*>(&As[buf][r * LW + lchunk * 8]) = ra[q];
+      *reinterpret_cast<uint4*>(&Bs[buf][r * LW + lchunk * 8]) = rb[q];
+    }
+  };
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int arow = wm * 32 + (lane & 31);
+  const int brow = wn * 32 + (lane & 31);
+  const int kofs = (lane >> 5) * 8;
+
+  f32x16_t acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+
+  const int64_t nstage = (ld + BK - 1) / BK;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int64_t st = 0; st < nstage; ++st) {
+    const int buf = static_cast<int>(st & 1);
+    if (st + 1 < nstage) load_stage((st + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&As[buf][arow * LW + kk * 16 + kofs]);
+      const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][brow * LW + kk * 16 + kofs]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+    }
+    if (st + 1 < nstage) {
+      store_stage(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // Accumulator element e of lane l holds row 8*(e/4) + 4*(l/32) + e%4,
+  // column l%32 of the wave's 32 x 32 sub-tile.
+  const int col = b0 + wn * 32 + (lane & 31);
+  if (col < b) {
+    float* gcol = Gj + static_cast<int64_t>(t) * b + col;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = a0 + wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (row < b) gcol[row * ldg] = acc[e];
+    }
+  }
+}
+
+// float32 storage: the same tiles on the vector ALUs (each lane a 4 x 4
+// register block), used when the data are kept in float32.
+__global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__ Y, int64_t ld,
+                                                       int s, int b, int tps,
+                                                       float* __restrict__ G, int64_t y_stride,
+                                                       int64_t g_stride) {
+  constexpr int BK = 16;
+  __shared__ float As[BK][kTile + 4];
+  __shared__ float Bs[BK][kTile + 4];
+  const int nt2 = tps * tps;
+  const int p = blockIdx.x / nt2;
+  const int rem = blockIdx.x - p * nt2;
+  const int ti = rem / tps;
+  const int tj = rem - ti * tps;
+  int j, t;
+  block_of(p, j, t);
+  (void)s;
+  const float* Yp = Y + static_cast<int64_t>(blockIdx.y) * y_stride;
+  float* Gj = G + static_cast<int64_t>(blockIdx.y) * g_stride +
+              static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
+  const int64_t ldg = static_cast<int64_t>(j) * b;
+  const int a0 = ti * kTile, b0 = tj * kTile;
+
+  // loader: 64 rows x 16 k per stage = 256 float4
+  const int lr = threadIdx.x >> 2;
+  const int lk = (threadIdx.x & 3) * 4;
+  const bool aok = a0 + lr < b, bok = b0 + lr < b;
+  const float* ap = Yp + (static_cast<int64_t>(j) * b + a0 + (aok ? lr : 0)) * ld + lk;
+  const float* bp = Yp + (static_cast<int64_t>(t) * b + b0 + (bok ? lr : 0)) * ld + lk;
+
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4] = {};
+  for (int64_t k0 = 0; k0 < ld; k0 += BK) {
+    const bool kin = k0 + lk < ld;
+    const float4 av = (aok && kin) ? *reinterpret_cast<const float4*>(ap + k0) : make_float4(0, 0, 0, 0);
+    const float4 bv = (bok && kin) ? *reinterpret_cast<const float4*>(bp + k0) : make_float4(0, 0, 0, 0);
+    As[lk + 0][lr] = av.x;
+    As[lk + 1][lr] = av.y;
+    As[lk + 2][lr] = av.z;
+    As[lk + 3][lr] = av.w;
+    Bs[lk + 0][lr] = bv.x;
+    Bs[lk + 1][lr] = bv.y;
+    Bs[lk + 2][lr] = bv.z;
+    Bs[lk + 3][lr] = bv.w;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < BK; ++k) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&As[k][ty * 4]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&Bs[k][tx * 4]);
+      const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[u][q] = fmaf(a[u], bb[q], acc[u][q]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = a0 + ty * 4 + u;
+    if (row >= b) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = b0 + tx * 4 + q;
+      if (col < b) Gj[row * ldg + static_cast<int64_t>(t) * b + col] = acc[u][q];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gram(int storage, const void* Y, int64_t ld, int s, int b, float* G, int nprob,
+                       int64_t y_stride, int64_t g_stride, hipStream_t st) {
+  const int nblocks = s * (s - 1) / 2;
+  if (nblocks == 0 || nprob == 0) return hipSuccess;
+  const int tps = (b + kTile - 1) / kTile;
+  const dim3 grid(static_cast<unsigned>(nblocks * tps * tps), static_cast<unsigned>(nprob));
+  if (storage == kStoreBF16) {
+    if (ld % 64 == 0 || ld > 32)
+      gram_bf16_kernel<64><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(Y), ld, s, b, tps, G,
+                                                  y_stride, g_stride);
+    else
+      gram_bf16_kernel<32><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(Y), ld, s, b, tps, G,
+                                                  y_stride, g_stride);
+  } else {
+    gram_f32_kernel<<<grid, 256, 0, st>>>(static_cast<const float*>(Y), ld, s, b, tps, G, y_stride,
+                                          g_stride);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace casgd

@@ -1,0 +1,132 @@
+// Mean loss over every stored row, f(w) = (1/m) sum_i l(x_i . w, y_i): the
+// quantity by which the Abstract of "Mixed-Precision Communication-Avoiding
+// SGD for Generalized Linear Models on GPUs" compares the method with float32
+// SGD.  Margins are float32 dot products of the stored rows; loss terms and
+// all sums are float64, reduced in a fixed order (no atomics).
+#include "casgd_device.h"
+#include "casgd_internal.h"
+
+namespace casgd {
+namespace {
+
+template <typename T>
+struct Widen;
+template <>
+struct Widen<uint16_t> {
+  static constexpr int kElems = 8;
+  __device__ static void run(const uint4& q, float (&f)[8]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
+      f[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+    }
+  }
+};
+template <>
+struct Widen<float> {
+  static constexpr int kElems = 4;
+  __device__ static void run(const uint4& q, float (&f)[4]) {
+    f[0] = __uint_as_float(q.x);
+    f[1] = __uint_as_float(q.y);
+    f[2] = __uint_as_float(q.z);
+    f[3] = __uint_as_float(q.w);
+  }
+};
+
+// Grid-stride over rows; a group of GS lanes per row.  Each block writes one
+// float64 partial sum.
+template <typename T, int LOSS, int GS>
+__global__ __launch_bounds__(256) void loss_kernel(const T* __restrict__ Xs,
+                                                   const float* __restrict__ y, int64_t m,
+                                                   int64_t n, int64_t ld,
+                                                   const float* __restrict__ w,
+                                                   double* __restrict__ partial) {
+  constexpr int E = Widen<T>::kElems;
+  const int lane = threadIdx.x % GS;
+  const int64_t groups = static_cast<int64_t>(gridDim.x) * (256 / GS);
+  const int64_t cpr = ld / E;
+  double acc = 0.0;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * (256 / GS) + threadIdx.x / GS; row < m;
+       row += groups) {
+    const uint4* xr = reinterpret_cast<const uint4*>(Xs + row * ld);
+    float d = 0.f;
+    for (int64_t c = lane; c < cpr; c += GS) {
+      float f[E];
+      Widen<T>::run(xr[c], f);
+      const int64_t col0 = c * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (col0 + e < n) d = fmaf(f[e], w[col0 + e], d);
+    }
+    d = group_sum<GS>(d);
+    if (lane == 0) acc += loss_value<LOSS>(static_cast<double>(d), static_cast<double>(y[row]));
+  }
+  __shared__ double red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void loss_finish_kernel(const double* __restrict__ partial, int np,
+                                                          double inv_m, double* __restrict__ out) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < np; i += 256) acc += partial[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = red[0] * inv_m;
+}
+
+template <typename T, int LOSS>
+void loss_gs(const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld, const float* w,
+             double* partial, hipStream_t st) {
+  const int64_t cpr = ld / Widen<T>::kElems;
+  const T* X = static_cast<const T*>(Xs);
+  if (cpr >= 64)
+    loss_kernel<T, LOSS, 64><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+  else if (cpr >= 32)
+    loss_kernel<T, LOSS, 32><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+  else if (cpr >= 16)
+    loss_kernel<T, LOSS, 16><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+  else if (cpr >= 8)
+    loss_kernel<T, LOSS, 8><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+  else
+    loss_kernel<T, LOSS, 4><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+}
+
+template <typename T>
+void loss_t(int loss, const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld,
+            const float* w, double* partial, hipStream_t st) {
+  if (loss == kLogistic)
+    loss_gs<T, kLogistic>(Xs, y, m, n, ld, w, partial, st);
+  else if (loss == kSquared)
+    loss_gs<T, kSquared>(Xs, y, m, n, ld, w, partial, st);
+  else
+    loss_gs<T, kPoisson>(Xs, y, m, n, ld, w, partial, st);
+}
+
+}  // namespace
+
+hipError_t launch_loss(int storage, int loss, const void* Xs, const float* y, int64_t m, int64_t n,
+                       int64_t ld, const float* w, double* partial, double* out_dev,
+                       hipStream_t st) {
+  if (storage == kStoreBF16)
+    loss_t<uint16_t>(loss, Xs, y, m, n, ld, w, partial, st);
+  else
+    loss_t<float>(loss, Xs, y, m, n, ld, w, partial, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  loss_finish_kernel<<<1, 256, 0, st>>>(partial, kLossBlocks, 1.0 / static_cast<double>(m), out_dev);
+  return hipGetLastError();
+}
+
+}  // namespace casgd

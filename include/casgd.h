@@ -1,0 +1,177 @@
+/*
+ * casgd.h - C ABI of the MI355X (gfx950) mixed-precision communication-avoiding
+ * SGD library for generalized linear models.
+ *
+ * Method: "Mixed-Precision Communication-Avoiding SGD for Generalized Linear
+ * Models on GPUs" (paperdance.org/p/2606.18463), Abstract.  One outer
+ * iteration replaces s minibatch SGD steps, each with its own AllReduce, by
+ * one sb x sb Gram matrix: the data matrix is stored in low precision
+ * (bfloat16), the Gram is formed from those low-precision rows with float32
+ * accumulation, and the inner recurrence and the weight update run in float32.
+ * Written out (the plain SGD step unrolled over s minibatches of b rows):
+ *
+ *   Y   = the s*b sampled rows of X, minibatch j = rows [j*b, (j+1)*b)
+ *   G_{j,t} = Y_j Y_t^T            for 0 <= t < j < s  (strictly-lower blocks)
+ *   v   = Y w0
+ *   z_j = v_j - (eta/b) sum_{t<j} G_{j,t} r_t,   r_j = l'(z_j, y_j)
+ *   w   = w0 - (eta/b) Y^T r
+ *
+ * Losses l(z, y): logistic log(1 + exp(-y z)) with y = +-1; squared
+ * (z - y)^2 / 2; Poisson exp(z) - y z.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are HIP device pointers on the current device;
+ *     "host" pointers are ordinary CPU memory.  No pointer is retained past
+ *     the call unless stated.
+ *   - Work is queued on the handle's stream (casgd_set_stream; default: the
+ *     null stream) and returns without waiting unless stated.
+ *   - Arguments are validated on the host before anything is queued; an
+ *     invalid call returns CASGD_EINVAL and changes nothing (w untouched).
+ *   - Errors: CASGD_EINVAL (bad argument), CASGD_ENOMEM (device allocation
+ *     failed), CASGD_EHIP (a HIP runtime call failed).  casgd_last_error()
+ *     returns a description of the last failure on the calling thread.
+ *   - NaN and Inf in the data or weights are not checked; they propagate.
+ *   - A handle is not thread-safe; distinct handles are independent.
+ */
+#ifndef CASGD_H
+#define CASGD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct casgd_ctx* casgd_handle;
+
+enum casgd_loss_kind { CASGD_LOGISTIC = 0, CASGD_SQUARED = 1, CASGD_POISSON = 2 };
+enum casgd_storage { CASGD_BF16 = 0, CASGD_FP32 = 1 };
+enum casgd_status { CASGD_OK = 0, CASGD_EINVAL = -1, CASGD_ENOMEM = -2, CASGD_EHIP = -3 };
+
+/* What casgd_debug_export copies out (state of the most recent outer step). */
+enum casgd_export_what {
+  CASGD_EXPORT_IDX = 0, /* int32[s*b]   sampled row indices                        */
+  CASGD_EXPORT_Y = 1,   /* stored type [s*b][ld]  gathered rows (bf16 bits or f32) */
+  CASGD_EXPORT_YB = 2,  /* float[s*b]   gathered labels / targets                  */
+  CASGD_EXPORT_G = 3,   /* float[b*b*s*(s-1)/2]  strictly-lower block triangle,     */
+                        /*   block-row layout: block-row j (1 <= j < s) is a       */
+                        /*   b x (j*b) row-major matrix [G_{j,0} ... G_{j,j-1}]    */
+                        /*   starting at element b*b*j*(j-1)/2                     */
+  CASGD_EXPORT_V = 4,   /* float[s*b]   margins v = Y w0                          */
+  CASGD_EXPORT_Z = 5,   /* float[s*b]   recurrence values z                       */
+  CASGD_EXPORT_R = 6    /* float[s*b]   loss derivatives r = l'(z, y)              */
+};
+
+/* Timers kept when timing is on (casgd_set_timing). */
+enum casgd_kernel_id {
+  CASGD_K_GATHER = 0, /* sample + gather + margins        */
+  CASGD_K_GRAM = 1,   /* strictly-lower Gram on MFMA      */
+  CASGD_K_RECUR = 2,  /* inner recurrence                 */
+  CASGD_K_UPDATE = 3, /* transposed-GEMV weight update    */
+  CASGD_K_COUNT = 4
+};
+
+/*
+ * Create a handle that owns the stored data.  The data matrix is the one the
+ * Abstract says is kept in low precision.
+ *   X      device, float32 [m][n] row-major contiguous; read during the call only
+ *   y      device, float32 [m]: labels +-1 (logistic), targets (squared),
+ *          counts (Poisson); read during the call only
+ *   m      rows, 1 <= m <= 2^31 - 1
+ *   n      features, n >= 1
+ *   loss   enum casgd_loss_kind
+ *   storage enum casgd_storage: CASGD_BF16 rounds X to bfloat16 (round to
+ *          nearest, ties to even); CASGD_FP32 keeps float32
+ * The stored rows are padded with zeros to ld = n rounded up to 32 elements.
+ * Synchronises the stream once so that failures surface here.
+ * Returns NULL on failure (see casgd_last_error).
+ */
+casgd_handle casgd_create(const float* X, const float* y, int64_t m, int64_t n,
+                          int loss, int storage);
+
+/* Free everything the handle owns.  NULL is allowed.  Synchronises its stream. */
+void casgd_destroy(casgd_handle h);
+
+/* Queue later work on hip_stream (a hipStream_t; NULL selects the null stream). */
+int casgd_set_stream(casgd_handle h, void* hip_stream);
+
+/*
+ * One CA-SGD outer iteration (s inner SGD steps), Abstract.
+ *   s, b   minibatches per outer step and rows per minibatch; 1 <= s,
+ *          1 <= b, s*b <= 16384
+ *   eta    learning rate (the step is eta/b times the minibatch sum)
+ *   seed   sampling seed of this outer step: row index i (i < s*b) is
+ *          floor(x_i * m / 2^64), x_i = output i of SplitMix64 seeded with seed
+ *   w      device, float32 [n]; read as w0, overwritten with the new weights
+ *          in stream order; must not alias handle memory
+ * Asynchronous.  Workspace grows on the first call with a larger s*b.
+ */
+int casgd_outer_step(casgd_handle h, int s, int b, float eta, uint64_t seed, float* w);
+
+/*
+ * As casgd_outer_step but with explicit row indices instead of sampling
+ * (for tests of degenerate minibatches).
+ *   idx    device, int32 [s*b], each in [0, m); copied to the host and
+ *          checked first, so this call synchronises the stream.
+ */
+int casgd_outer_step_indices(casgd_handle h, int s, int b, float eta,
+                             const int32_t* idx, float* w);
+
+/*
+ * n_outer consecutive outer iterations; outer step k (k = first_step ...
+ * first_step + n_outer - 1) samples with seed casgd_step_seed(base_seed, k).
+ * Equivalent to calling casgd_outer_step with those seeds.  Asynchronous.
+ */
+int casgd_train(casgd_handle h, int s, int b, float eta, uint64_t base_seed,
+                uint64_t first_step, int n_outer, float* w);
+
+/* Seed of outer step k: output k of SplitMix64 seeded with base_seed. */
+uint64_t casgd_step_seed(uint64_t base_seed, uint64_t k);
+
+/*
+ * Mean loss over every stored row, f(w) = (1/m) sum_i l(x_i . w, y_i): float32
+ * dot products, float64 loss terms and sums (the Abstract compares methods by
+ * this loss).  w: device float32 [n].  out: host double.  Synchronises.
+ */
+int casgd_loss(casgd_handle h, const float* w, double* out);
+
+/*
+ * Copy part of the most recent outer step's state to host memory (tests and
+ * benchmarks).  what: enum casgd_export_what; bytes must equal the exact size
+ * of that array.  Synchronises the stream.
+ */
+int casgd_debug_export(casgd_handle h, int what, void* dst_host, size_t bytes);
+
+/* Copy stored rows [row0, row0 + nrows) (bf16 bits or float32, ld wide) to
+ * host memory; bytes must equal nrows * ld * element size.  Synchronises. */
+int casgd_export_rows(casgd_handle h, int64_t row0, int64_t nrows, void* dst_host,
+                      size_t bytes);
+
+/* Padded row length (elements) of the stored data. */
+int64_t casgd_ld(casgd_handle h);
+
+/*
+ * Bytes of the float32 Gram that the one AllReduce per outer step would carry
+ * between processes (Abstract): packed != 0 gives the strictly-lower block
+ * triangle (4 * b*b * s*(s-1)/2), packed == 0 the full sb x sb matrix.
+ * On one process the AllReduce itself is omitted.  Returns -1 on bad input.
+ */
+int64_t casgd_gram_bytes(int s, int b, int packed);
+
+/* Time every kernel launch with HIP events on the handle's stream (on != 0). */
+int casgd_set_timing(casgd_handle h, int on);
+
+/* Total milliseconds and launch count of one kernel (enum casgd_kernel_id)
+ * since timing was switched on; synchronises.  reset != 0 clears it after. */
+int casgd_get_timing(casgd_handle h, int kernel, double* total_ms, int64_t* launches,
+                     int reset);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* casgd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CASGD_H */

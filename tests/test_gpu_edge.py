@@ -1,0 +1,187 @@
+"""Edge cases of the GPU path through the C ABI: degenerate shapes, ragged
+tiles, the largest s*b, explicit and duplicated indices, orthogonal rows,
+argument errors, determinism, resume, and streams."""
+
+import numpy as np
+import pytest
+
+from communication_avoiding_mixed_amd import binding as B
+from communication_avoiding_mixed_amd import synth
+from oracle import casgd_oracle as O
+
+from gpu_common import REL_TOL, check_gram, rel_l2, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _targets(loss, m, seed):
+    rng = np.random.default_rng(seed)
+    if loss == "logistic":
+        return np.where(rng.random(m) < 0.5, -1.0, 1.0).astype(np.float32)
+    if loss == "squared":
+        return rng.standard_normal(m).astype(np.float32)
+    return rng.poisson(1.0, m).astype(np.float32)
+
+
+def run_and_compare(X, y, loss, s, b, eta, w0, seed=123, storage="bf16", idx=None):
+    import torch
+    h = B.CASGD(torch_dev(X), torch_dev(y), loss, storage)
+    w = torch_dev(w0)
+    if idx is None:
+        h.outer_step(s, b, eta, seed, w)
+    else:
+        h.outer_step_indices(s, b, eta, torch.from_numpy(np.asarray(idx, np.int32)).cuda(), w)
+    ref = O.outer_step(X, y, w0.astype(np.float64), s, b, eta, seed, loss, storage=storage, idx=idx)
+    assert np.array_equal(h.export(B.EXPORT_IDX).astype(np.int64), ref["idx"])
+    errs = {
+        "G": check_gram(h.export(B.EXPORT_G), ref["Y"], s, b, X.shape[1]),
+        "v": rel_l2(h.export(B.EXPORT_V), ref["v"]),
+        "z": rel_l2(h.export(B.EXPORT_Z), ref["z"]),
+        "r": rel_l2(h.export(B.EXPORT_R), ref["r"]),
+        "w": rel_l2(w.cpu().numpy(), ref["w"]),
+    }
+    for k, e in errs.items():
+        assert e <= REL_TOL, (k, e, s, b, X.shape)
+    return h, w, ref
+
+
+@pytest.mark.parametrize("loss", ["logistic", "squared", "poisson"])
+@pytest.mark.parametrize("m,n,s,b", [
+    (500, 70, 3, 48),    # b not a multiple of the 64-row tile, ld 96
+    (300, 33, 4, 100),   # ragged tiles on both sides, ld 64
+    (200, 1, 5, 7),      # one feature, tiny blocks
+    (1000, 130, 2, 130),  # tiles crossing the block edge, ld 160 (K tail)
+    (64, 32, 1, 64),     # s = 1: no Gram at all
+    (1, 16, 3, 5),       # one row: every index is 0
+    (700, 200, 9, 1),    # b = 1: 1 x 1 blocks
+])
+def test_ragged_and_degenerate_shapes(loss, m, n, s, b):
+    X = synth.make_uniform((m, n), seed=m + n, lo=-0.5, hi=0.5)
+    y = _targets(loss, m, seed=s)
+    w0 = synth.make_uniform((n,), seed=7, lo=-0.3, hi=0.3)
+    h, w, ref = run_and_compare(X, y, loss, s, b, 0.3, w0)
+    if s == 1:
+        assert h.export(B.EXPORT_G).size == 0
+        assert np.array_equal(h.export(B.EXPORT_Z), h.export(B.EXPORT_V))
+
+
+def test_fp32_storage_ragged():
+    X = synth.make_uniform((400, 45), seed=3)
+    y = _targets("logistic", 400, 1)
+    run_and_compare(X, y, "logistic", 5, 24, 0.5, synth.make_uniform((45,), seed=4), storage="fp32")
+
+
+@pytest.mark.parametrize("s,b", [(2, 8192), (128, 128)])
+def test_largest_minibatch_set(s, b):
+    # s*b = 16384, the library's limit
+    X = synth.make_uniform((5000, 24), seed=11, lo=-0.2, hi=0.2)
+    y = _targets("squared", 5000, 2)
+    run_and_compare(X, y, "squared", s, b, 0.01, np.zeros(24, np.float32))
+
+
+def test_orthogonal_rows_give_zero_gram():
+    n = 64
+    X = np.eye(n, dtype=np.float32)
+    y = _targets("logistic", n, 5)
+    idx = np.random.default_rng(0).permutation(n)[:48]
+    w0 = synth.make_uniform((n,), seed=9)
+    h, w, ref = run_and_compare(X, y, "logistic", 3, 16, 0.5, w0, idx=idx)
+    assert not np.any(h.export(B.EXPORT_G))
+    c = float(np.float32(0.5)) / 16
+    expect = w0.astype(np.float64).copy()
+    for i in idx:
+        expect[i] -= c * O.loss_derivative(float(w0[i]), float(y[i]), "logistic")[0]
+    assert rel_l2(w.cpu().numpy(), expect) <= 1e-6
+
+
+def test_duplicated_indices():
+    X = synth.make_uniform((50, 40), seed=12)
+    y = _targets("poisson", 50, 3)
+    idx = np.array([7] * 32 + [3] * 32)
+    run_and_compare(X, y, "poisson", 4, 16, 0.05, synth.make_uniform((40,), seed=1, lo=-.2, hi=.2), idx=idx)
+
+
+def test_invalid_arguments_leave_w_untouched():
+    import torch
+    X = synth.make_uniform((100, 10), seed=1)
+    y = _targets("logistic", 100, 1)
+    h = B.CASGD(torch_dev(X), torch_dev(y), "logistic")
+    w = torch.ones(10, device="cuda")
+    lib = B.load()
+    hh = h._handle()
+    wp = B.ctypes.c_void_p(w.data_ptr())
+    assert lib.casgd_outer_step(hh, 0, 4, 0.1, 0, wp) == B.EINVAL
+    assert lib.casgd_outer_step(hh, 4, 0, 0.1, 0, wp) == B.EINVAL
+    assert lib.casgd_outer_step(hh, 129, 128, 0.1, 0, wp) == B.EINVAL
+    assert lib.casgd_outer_step(hh, 2, 2, 0.1, 0, None) == B.EINVAL
+    bad = torch.tensor([0, 1, 100, 2], dtype=torch.int32, device="cuda")
+    assert lib.casgd_outer_step_indices(hh, 2, 2, 0.1, B.ctypes.c_void_p(bad.data_ptr()), wp) == B.EINVAL
+    neg = torch.tensor([0, -1, 1, 2], dtype=torch.int32, device="cuda")
+    assert lib.casgd_outer_step_indices(hh, 2, 2, 0.1, B.ctypes.c_void_p(neg.data_ptr()), wp) == B.EINVAL
+    assert lib.casgd_debug_export(hh, B.EXPORT_V, None, 0) == B.EINVAL
+    assert lib.casgd_export_rows(hh, 99, 2, B.ctypes.c_void_p(1), 10) == B.EINVAL
+    assert lib.casgd_get_timing(hh, 9, None, None, 0) == B.EINVAL
+    torch.cuda.synchronize()
+    assert torch.equal(w, torch.ones(10, device="cuda"))
+    # the handle still works afterwards
+    h.outer_step(2, 2, 0.1, 0, w)
+    assert np.all(np.isfinite(w.cpu().numpy()))
+    with pytest.raises(B.CasgdError):
+        h.export_rows(0, 101)
+    assert not lib.casgd_create(B.ctypes.c_void_p(w.data_ptr()), B.ctypes.c_void_p(w.data_ptr()), 0, 5, 0, 0)
+    assert not lib.casgd_create(B.ctypes.c_void_p(w.data_ptr()), B.ctypes.c_void_p(w.data_ptr()), 2, 5, 7, 0)
+    assert not lib.casgd_create(B.ctypes.c_void_p(w.data_ptr()), B.ctypes.c_void_p(w.data_ptr()), 2, 5, 0, 9)
+
+
+def test_nonfinite_values_propagate_without_failure():
+    import torch
+    X = synth.make_uniform((200, 16), seed=2, lo=0.5, hi=1.0)
+    y = _targets("poisson", 200, 4)
+    h = B.CASGD(torch_dev(X), torch_dev(y), "poisson")
+    w = torch.full((16,), 50.0, device="cuda")
+    h.outer_step(4, 8, 1e4, 1, w)
+    val = h.loss_value(w)
+    assert not np.isfinite(val) or val > 1e10
+
+
+def test_repeatable_and_resumable():
+    import torch
+    name = "poisson-synth"
+    wl = synth.WORKLOADS[name]
+    X, y = synth.make_data(name, m=30_000)
+    h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss)
+    w1 = torch.zeros(wl.n, device="cuda")
+    h.train(wl.s, wl.b, wl.eta, 0, 0, 20, w1)
+    w2 = torch.zeros(wl.n, device="cuda")
+    h.train(wl.s, wl.b, wl.eta, 0, 0, 20, w2)
+    assert torch.equal(w1, w2)
+    w3 = torch.zeros(wl.n, device="cuda")
+    h.train(wl.s, wl.b, wl.eta, 0, 0, 10, w3)
+    saved = w3.clone()
+    w4 = saved.clone()
+    h.train(wl.s, wl.b, wl.eta, 0, 10, 10, w4)
+    assert torch.equal(w4, w1)
+    w5 = torch.zeros(wl.n, device="cuda")
+    for k in range(20):
+        h.outer_step(wl.s, wl.b, wl.eta, O.step_seed(0, k), w5)
+    assert torch.equal(w5, w1)
+
+
+def test_side_stream_and_timing():
+    import torch
+    name = "logistic-4096x64"
+    wl = synth.WORKLOADS[name]
+    X, y = synth.make_data(name)
+    h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss)
+    w_ref = torch.zeros(wl.n, device="cuda")
+    h.train(wl.s, wl.b, wl.eta, 0, 0, 5, w_ref)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        w = torch.zeros(wl.n, device="cuda")
+        h.set_timing(True)
+        h.train(wl.s, wl.b, wl.eta, 0, 0, 5, w)
+        ms, cnt = h.timing(B.K_GRAM)
+        h.set_timing(False)
+    side.synchronize()
+    assert torch.equal(w, w_ref)
+    assert cnt == 5 and ms > 0

@@ -1,0 +1,86 @@
+"""The five workloads at their full sizes, in the launch configuration the
+benchmark times, through the C ABI.
+
+Per workload: sampled indices and gathered rows bit-exact; one outer step from
+seeded weights within relative L2 1e-4 of the oracle for G, v, z, r and w
+(the oracle only needs the s*b sampled rows, so this is exact at any m); the
+loss at w = 0 against its closed form and at the seeded weights against the
+oracle; and the whole run (20 or 200 outer steps from w = 0) ending within
+0.5% of the loss of float64 SGD on the float32 data over the same minibatches.
+"""
+
+import math
+import time
+
+import numpy as np
+import pytest
+
+from communication_avoiding_mixed_amd import binding as B
+from communication_avoiding_mixed_amd import synth
+from oracle import casgd_oracle as O
+
+from gpu_common import LOSS_GAP, REL_TOL, check_gram, rel_l2, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def closed_form_loss_at_zero(loss, y):
+    if loss == "logistic":
+        return math.log(2.0)
+    if loss == "squared":
+        return 0.5 * float(np.mean(np.asarray(y, np.float64) ** 2))
+    return 1.0
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_full_size_workload(name):
+    import torch
+    t0 = time.time()
+    wl = synth.WORKLOADS[name]
+    X, y = synth.make_data(name)
+    h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss, wl.storage)
+    t_gen = time.time() - t0
+
+    # one outer step from seeded weights
+    w0 = synth.make_w0(name, 3)
+    w = torch_dev(w0)
+    seed = O.step_seed(0, 11)
+    h.outer_step(wl.s, wl.b, wl.eta, seed, w)
+    ref = O.outer_step(X, y, w0.astype(np.float64), wl.s, wl.b, wl.eta, seed, wl.loss)
+    assert np.array_equal(h.export(B.EXPORT_IDX).astype(np.int64), ref["idx"])
+    Yg = h.export(B.EXPORT_Y)
+    expect = np.zeros_like(Yg)
+    expect[:, :wl.n] = O.bf16_bits(X[ref["idx"]])
+    assert np.array_equal(Yg, expect)
+    errs = {
+        "G": check_gram(h.export(B.EXPORT_G), ref["Y"], wl.s, wl.b, wl.n),
+        "v": rel_l2(h.export(B.EXPORT_V), ref["v"]),
+        "z": rel_l2(h.export(B.EXPORT_Z), ref["z"]),
+        "r": rel_l2(h.export(B.EXPORT_R), ref["r"]),
+        "w": rel_l2(w.cpu().numpy(), ref["w"]),
+    }
+    for k, e in errs.items():
+        assert e <= REL_TOL, (k, e)
+
+    # loss: closed form at zero, oracle at the seeded weights
+    zero = torch.zeros(wl.n, device="cuda")
+    f0 = h.loss_value(zero)
+    assert abs(f0 - closed_form_loss_at_zero(wl.loss, y)) <= REL_TOL * abs(f0)
+    f_seeded = h.loss_value(torch_dev(w0))
+    f_seeded_ref = O.full_loss(X, y, w0.astype(np.float64), wl.loss, storage="bf16")
+    assert abs(f_seeded - f_seeded_ref) <= REL_TOL * abs(f_seeded_ref)
+
+    # whole run from zero vs float64 SGD on the float32 data
+    wt = torch.zeros(wl.n, device="cuda")
+    h.train(wl.s, wl.b, wl.eta, 0, 0, wl.outer, wt)
+    f_gpu = h.loss_value(wt)
+    w_sgd = O.train(X, y, np.zeros(wl.n), wl.s, wl.b, wl.eta, wl.loss, base_seed=0,
+                    n_outer=wl.outer, storage="fp32", method="sgd")
+    f_ref = O.full_loss(X, y, w_sgd, wl.loss, storage="fp32")
+    gap = abs(f_gpu - f_ref) / abs(f_ref)
+    print(f"{name}: step errs {({k: f'{v:.1e}' for k, v in errs.items()})} "
+          f"final loss gpu {f_gpu:.6f} sgd64 {f_ref:.6f} gap {gap:.2e} "
+          f"(start {f0:.4f}); data {t_gen:.0f}s total {time.time() - t0:.0f}s", flush=True)
+    assert f_gpu < f0
+    assert gap <= LOSS_GAP
+    h.close()
