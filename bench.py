@@ -35,10 +35,10 @@ def algorithmic(wl):
     g_bytes = 2 * b * b * s * (s - 1)              # packed float32 G
     return {
         "gram_flops": gram_flops,
-        "gather_bytes": sb * n * 2 + sb * 12 + n * 4,   # rows read, idx/yB/v, w
+        "gather_bytes": sb * n * 2 + sb * 12,           # rows read, idx/yB
         "gram_bytes": sb * n * 2 + g_bytes,             # Y read, G written
-        "recur_bytes": g_bytes + sb * 16,               # G read, v/yB in, z/r out
-        "update_bytes": sb * n * 2 + sb * 4 + 2 * n * 4,  # Y read, r, w read+write
+        # margins (Y read), recurrence (G read), update (Y read), vectors
+        "chain_bytes": 2 * sb * n * 2 + g_bytes + sb * 20 + 3 * n * 4,
         "B_A": sb * n * 2 + g_bytes,
         "B_B": g_bytes,
         "B_C": sb * n * 2 + 2 * n * 4,
@@ -134,8 +134,7 @@ def main():
         "gather": {"us": per["gather"], "GB/s": alg["gather_bytes"] / (per["gather"] * 1e-6) / 1e9},
         "gram": {"us": per["gram"], "TFLOP/s": gram_tflops,
                  "GB/s": alg["gram_bytes"] / (per["gram"] * 1e-6) / 1e9},
-        "recur": {"us": per["recur"], "GB/s": alg["recur_bytes"] / (per["recur"] * 1e-6) / 1e9},
-        "update": {"us": per["update"], "GB/s": alg["update_bytes"] / (per["update"] * 1e-6) / 1e9},
+        "chain": {"us": per["chain"], "GB/s": alg["chain_bytes"] / (per["chain"] * 1e-6) / 1e9},
     }
     for k in kernels.values():
         for u in list(k):

@@ -20,8 +20,8 @@ LOGISTIC, SQUARED, POISSON = 0, 1, 2
 BF16, FP32 = 0, 1
 OK, EINVAL, ENOMEM, EHIP = 0, -1, -2, -3
 EXPORT_IDX, EXPORT_Y, EXPORT_YB, EXPORT_G, EXPORT_V, EXPORT_Z, EXPORT_R = range(7)
-K_GATHER, K_GRAM, K_RECUR, K_UPDATE = range(4)
-KERNEL_NAMES = {K_GATHER: "gather", K_GRAM: "gram", K_RECUR: "recur", K_UPDATE: "update"}
+K_GATHER, K_GRAM, K_CHAIN = range(3)
+KERNEL_NAMES = {K_GATHER: "gather", K_GRAM: "gram", K_CHAIN: "chain"}
 
 LOSS_IDS = {"logistic": LOGISTIC, "squared": SQUARED, "poisson": POISSON}
 STORAGE_IDS = {"bf16": BF16, "fp32": FP32}

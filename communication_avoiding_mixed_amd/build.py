@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcasgd.so")
 
-SOURCES = ["casgd_api.hip", "k_gather.hip", "k_gram.hip", "k_recur_update.hip", "k_loss.hip"]
+SOURCES = ["casgd_api.hip", "k_gather.hip", "k_gram.hip", "k_chain.hip", "k_loss.hip"]
 HEADERS = ["casgd_device.h", "casgd_internal.h"]
 
 ARCH = "gfx950"

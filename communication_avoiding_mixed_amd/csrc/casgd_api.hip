@@ -1,8 +1,15 @@
 // C ABI of the CA-SGD library: argument checks, handle-owned device memory,
-// stream handling, optional per-kernel event timing, and the sequence of
-// launches that makes one outer iteration (Abstract of "Mixed-Precision
-// Communication-Avoiding SGD for Generalized Linear Models on GPUs"):
-// sample + gather + margins, strictly-lower Gram, inner recurrence, update.
+// streams, optional per-kernel event timing, and the launches that make one
+// outer iteration (Abstract of "Mixed-Precision Communication-Avoiding SGD for
+// Generalized Linear Models on GPUs").
+//
+// An outer iteration is split at its only weight dependence.  Sampling,
+// gathering and the Gram matrix depend on the seed alone; they run on the
+// handle's internal "prep" stream into one of two buffer sets.  Margins, the
+// inner recurrence and the update need the weights; they run as one kernel on
+// the caller's stream once the step's prep is done.  Consecutive steps
+// alternate buffer sets, so the next step's gather and Gram overlap the
+// current step's recurrence.
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -34,6 +41,13 @@ struct EventPair {
   hipEvent_t stop = nullptr;
 };
 
+struct StepBuffers {
+  int32_t* idx = nullptr;
+  void* Y = nullptr;
+  float* yB = nullptr;
+  float* G = nullptr;
+};
+
 }  // namespace
 
 struct casgd_ctx {
@@ -42,25 +56,29 @@ struct casgd_ctx {
   size_t esize = 0;
   void* Xs = nullptr;
   float* y = nullptr;
-  hipStream_t stream = nullptr;
+  hipStream_t stream = nullptr;  // caller's stream: weight-dependent work
+  hipStream_t prep = nullptr;    // internal: sampling, gather, Gram
+  hipEvent_t ev_prep[2] = {nullptr, nullptr};
+  hipEvent_t ev_chain[2] = {nullptr, nullptr};
 
   // workspace, sized for cap_sb rows and cap_g Gram elements
   int cap_sb = 0;
   int64_t cap_g = 0;
-  int32_t* idx = nullptr;
-  void* Y = nullptr;
-  float* yB = nullptr;
-  float* G = nullptr;
+  StepBuffers buf[2];
   float* v = nullptr;
   float* z = nullptr;
   float* r = nullptr;
+  int32_t* idx_user = nullptr;
+  unsigned long long* xbuf = nullptr;
+  int* status = nullptr;
   double* loss_partial = nullptr;
   double* loss_out = nullptr;
+  uint32_t epoch = 0;
 
-  // shape of the most recent outer step (for exports)
+  int next_buf = 0;
+  int last_buf = 0;
   int last_s = 0, last_b = 0;
 
-  // timing
   bool timing = false;
   std::vector<EventPair> pending[CASGD_K_COUNT];
   std::vector<EventPair> pool;
@@ -70,37 +88,64 @@ struct casgd_ctx {
 
 namespace {
 
+template <typename P>
+void release(P*& p) {
+  if (p) (void)hipFree(p);
+  p = nullptr;
+}
+
 void free_workspace(casgd_ctx* h) {
-  (void)hipFree(h->idx);
-  (void)hipFree(h->Y);
-  (void)hipFree(h->yB);
-  (void)hipFree(h->G);
-  (void)hipFree(h->v);
-  (void)hipFree(h->z);
-  (void)hipFree(h->r);
-  h->idx = nullptr;
-  h->Y = nullptr;
-  h->yB = h->G = h->v = h->z = h->r = nullptr;
+  for (auto& bset : h->buf) {
+    release(bset.idx);
+    release(bset.Y);
+    release(bset.yB);
+    release(bset.G);
+  }
+  release(h->v);
+  release(h->z);
+  release(h->r);
+  release(h->idx_user);
+  release(h->xbuf);
   h->cap_sb = 0;
   h->cap_g = 0;
+}
+
+hipError_t sync_all(casgd_ctx* h) {
+  hipError_t e = hipStreamSynchronize(h->prep);
+  hipError_t e2 = hipStreamSynchronize(h->stream);
+  return e != hipSuccess ? e : e2;
+}
+
+template <typename P>
+bool grab(P*& p, size_t bytes) {
+  void* q = nullptr;
+  if (hipMalloc(&q, bytes > 0 ? bytes : 16) != hipSuccess) return false;
+  p = static_cast<P*>(q);
+  return true;
 }
 
 int ensure_workspace(casgd_ctx* h, int s, int b) {
   const int sb = s * b;
   const int64_t gsz = static_cast<int64_t>(b) * b * s * (s - 1) / 2;
   if (sb <= h->cap_sb && gsz <= h->cap_g) return CASGD_OK;
-  hipError_t e = hipStreamSynchronize(h->stream);
+  hipError_t e = sync_all(h);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   const int new_sb = sb > h->cap_sb ? sb : h->cap_sb;
   const int64_t new_g = gsz > h->cap_g ? gsz : h->cap_g;
   free_workspace(h);
-  bool ok = hipMalloc(&h->idx, sizeof(int32_t) * new_sb) == hipSuccess &&
-            hipMalloc(&h->Y, h->esize * h->ld * new_sb) == hipSuccess &&
-            hipMalloc(&h->yB, sizeof(float) * new_sb) == hipSuccess &&
-            hipMalloc(&h->G, sizeof(float) * (new_g > 0 ? new_g : 1)) == hipSuccess &&
-            hipMalloc(&h->v, sizeof(float) * new_sb) == hipSuccess &&
-            hipMalloc(&h->z, sizeof(float) * new_sb) == hipSuccess &&
-            hipMalloc(&h->r, sizeof(float) * new_sb) == hipSuccess;
+  bool ok = true;
+  for (auto& bset : h->buf) {
+    ok = ok && grab(bset.idx, sizeof(int32_t) * new_sb) && grab(bset.Y, h->esize * h->ld * new_sb) &&
+         grab(bset.yB, sizeof(float) * new_sb) && grab(bset.G, sizeof(float) * new_g);
+  }
+  ok = ok && grab(h->v, sizeof(float) * new_sb) && grab(h->z, sizeof(float) * new_sb) &&
+       grab(h->r, sizeof(float) * new_sb) && grab(h->idx_user, sizeof(int32_t) * new_sb) &&
+       grab(h->xbuf, sizeof(unsigned long long) * casgd::kChainMaxWorkgroups * new_sb);
+  if (ok) {
+    ok = hipMemset(h->xbuf, 0, sizeof(unsigned long long) * casgd::kChainMaxWorkgroups * new_sb) ==
+             hipSuccess &&
+         hipDeviceSynchronize() == hipSuccess;
+  }
   if (!ok) {
     (void)hipGetLastError();
     free_workspace(h);
@@ -123,14 +168,14 @@ EventPair take_pair(casgd_ctx* h) {
   return p;
 }
 
-// Launch `fn` on the handle's stream, bracketed by events when timing is on.
+// Launch `fn` on `st`, bracketed by events when timing is on.
 template <typename Fn>
-hipError_t timed(casgd_ctx* h, int kernel, Fn&& fn) {
+hipError_t timed(casgd_ctx* h, int kernel, hipStream_t st, Fn&& fn) {
   if (!h->timing) return fn();
   EventPair p = take_pair(h);
-  (void)hipEventRecord(p.start, h->stream);
+  (void)hipEventRecord(p.start, st);
   hipError_t e = fn();
-  (void)hipEventRecord(p.stop, h->stream);
+  (void)hipEventRecord(p.stop, st);
   h->pending[kernel].push_back(p);
   return e;
 }
@@ -143,6 +188,18 @@ int check_step_args(casgd_ctx* h, int s, int b, const float* w) {
   return CASGD_OK;
 }
 
+// Check the kernels' error word (exchange waits that expired); streams are synced.
+int check_status(casgd_ctx* h) {
+  int st = 0;
+  hipError_t e = hipMemcpy(&st, h->status, sizeof(int), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the status word");
+  if (st != 0) {
+    (void)hipMemset(h->status, 0, sizeof(int));
+    return fail(CASGD_EHIP, "an inner-step exchange between workgroups timed out");
+  }
+  return CASGD_OK;
+}
+
 // The launches of one outer iteration.  idx_in == nullptr: sample with `seed`.
 int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_t* idx_in,
               float* w) {
@@ -150,24 +207,54 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   if (rc != CASGD_OK) return rc;
   const int sb = s * b;
   const float c = eta / static_cast<float>(b);
+  const int k = h->next_buf;
+  StepBuffers& B = h->buf[k];
   hipError_t e;
-  e = timed(h, CASGD_K_GATHER, [&] {
-    return casgd::launch_gather(h->storage, h->Xs, h->y, h->m, h->n, h->ld, sb, seed, idx_in,
-                                h->idx, h->Y, h->yB, w, h->v, h->stream);
+
+  // weight-independent part, on the prep stream
+  e = hipStreamWaitEvent(h->prep, h->ev_chain[k], 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  e = timed(h, CASGD_K_GATHER, h->prep, [&] {
+    return casgd::launch_gather(h->storage, h->Xs, h->y, h->m, h->ld, sb, seed, idx_in, B.idx,
+                                B.Y, B.yB, h->prep);
   });
   if (e != hipSuccess) return hip_fail(e, "gather launch");
-  e = timed(h, CASGD_K_GRAM, [&] {
-    return casgd::launch_gram(h->storage, h->Y, h->ld, s, b, h->G, 1, 0, 0, h->stream);
+  const casgd::GramPlan plan = casgd::gram_plan(h->storage, s, b, h->ld);
+  e = timed(h, CASGD_K_GRAM, h->prep, [&] {
+    return casgd::launch_gram(h->storage, B.Y, h->ld, s, b, B.G, plan, h->prep);
   });
   if (e != hipSuccess) return hip_fail(e, "gram launch");
-  e = timed(h, CASGD_K_RECUR, [&] {
-    return casgd::launch_recur(h->loss, h->G, h->v, h->yB, h->z, h->r, s, b, c, h->stream);
-  });
+  e = hipEventRecord(h->ev_prep[k], h->prep);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+  // weight-dependent part, on the caller's stream
+  e = hipStreamWaitEvent(h->stream, h->ev_prep[k], 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  casgd::ChainArgs a;
+  a.Y = B.Y;
+  a.ld = h->ld;
+  a.n = h->n;
+  a.s = s;
+  a.b = b;
+  a.Q = casgd::chain_workgroups(s, b);
+  a.c = c;
+  a.G = B.G;
+  a.yB = B.yB;
+  a.v = h->v;
+  a.z = h->z;
+  a.r = h->r;
+  a.w = w;
+  a.xbuf = h->xbuf;
+  a.epoch = ++h->epoch == 0 ? ++h->epoch : h->epoch;
+  a.status = h->status;
+  e = timed(h, CASGD_K_CHAIN, h->stream,
+            [&] { return casgd::launch_chain(h->storage, h->loss, a, h->stream); });
   if (e != hipSuccess) return hip_fail(e, "recurrence launch");
-  e = timed(h, CASGD_K_UPDATE, [&] {
-    return casgd::launch_update(h->storage, h->Y, h->ld, h->n, sb, h->r, c, w, h->stream);
-  });
-  if (e != hipSuccess) return hip_fail(e, "update launch");
+  e = hipEventRecord(h->ev_chain[k], h->stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+  h->last_buf = k;
+  h->next_buf = k ^ 1;
   h->last_s = s;
   h->last_b = b;
   return CASGD_OK;
@@ -213,16 +300,26 @@ casgd_handle casgd_create(const float* X, const float* y, int64_t m, int64_t n, 
   h->loss = loss;
   h->storage = storage;
   h->esize = storage == CASGD_BF16 ? 2 : 4;
-  if (hipMalloc(&h->Xs, h->esize * h->ld * m) != hipSuccess ||
-      hipMalloc(&h->y, sizeof(float) * m) != hipSuccess ||
-      hipMalloc(&h->loss_partial, sizeof(double) * casgd::kLossBlocks) != hipSuccess ||
-      hipMalloc(&h->loss_out, sizeof(double)) != hipSuccess) {
+  bool ok = hipStreamCreateWithFlags(&h->prep, hipStreamNonBlocking) == hipSuccess;
+  for (int i = 0; i < 2 && ok; ++i)
+    ok = hipEventCreateWithFlags(&h->ev_prep[i], hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&h->ev_chain[i], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    fail(CASGD_EHIP, "creating the handle's stream and events failed");
+    casgd_destroy(h);
+    return nullptr;
+  }
+  if (!grab(h->Xs, h->esize * h->ld * m) || !grab(h->y, sizeof(float) * m) ||
+      !grab(h->loss_partial, sizeof(double) * casgd::kLossBlocks) ||
+      !grab(h->loss_out, sizeof(double)) || !grab(h->status, sizeof(int))) {
     (void)hipGetLastError();
     fail(CASGD_ENOMEM, "device allocation of the stored data failed");
     casgd_destroy(h);
     return nullptr;
   }
-  hipError_t e = casgd::launch_store(storage, X, h->Xs, m, n, h->ld, h->stream);
+  hipError_t e = hipMemsetAsync(h->status, 0, sizeof(int), h->stream);
+  if (e == hipSuccess) e = casgd::launch_store(storage, X, h->Xs, m, n, h->ld, h->stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(h->y, y, sizeof(float) * m, hipMemcpyDeviceToDevice, h->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
@@ -236,18 +333,25 @@ casgd_handle casgd_create(const float* X, const float* y, int64_t m, int64_t n, 
 
 void casgd_destroy(casgd_handle h) {
   if (!h) return;
+  if (h->prep) (void)hipStreamSynchronize(h->prep);
   (void)hipStreamSynchronize(h->stream);
   free_workspace(h);
-  (void)hipFree(h->Xs);
-  (void)hipFree(h->y);
-  (void)hipFree(h->loss_partial);
-  (void)hipFree(h->loss_out);
+  release(h->Xs);
+  release(h->y);
+  release(h->loss_partial);
+  release(h->loss_out);
+  release(h->status);
   for (auto& v : h->pending)
     for (auto& p : v) h->pool.push_back(p);
   for (auto& p : h->pool) {
     (void)hipEventDestroy(p.start);
     (void)hipEventDestroy(p.stop);
   }
+  for (int i = 0; i < 2; ++i) {
+    if (h->ev_prep[i]) (void)hipEventDestroy(h->ev_prep[i]);
+    if (h->ev_chain[i]) (void)hipEventDestroy(h->ev_chain[i]);
+  }
+  if (h->prep) (void)hipStreamDestroy(h->prep);
   delete h;
 }
 
@@ -278,7 +382,14 @@ int casgd_outer_step_indices(casgd_handle h, int s, int b, float eta, const int3
   if (e != hipSuccess) return hip_fail(e, "copying indices");
   for (int i = 0; i < sb; ++i)
     if (host[i] < 0 || host[i] >= h->m) return fail(CASGD_EINVAL, "row index out of range");
-  return run_outer(h, s, b, eta, 0, idx, w);
+  rc = ensure_workspace(h, s, b);
+  if (rc != CASGD_OK) return rc;
+  // the previous step's gather may still read idx_user
+  e = hipStreamSynchronize(h->prep);
+  if (e == hipSuccess)
+    e = hipMemcpy(h->idx_user, host.data(), sizeof(int32_t) * sb, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "copying indices");
+  return run_outer(h, s, b, eta, 0, h->idx_user, w);
 }
 
 int casgd_train(casgd_handle h, int s, int b, float eta, uint64_t base_seed, uint64_t first_step,
@@ -300,9 +411,9 @@ int casgd_loss(casgd_handle h, const float* w, double* out) {
                                     h->loss_partial, h->loss_out, h->stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(out, h->loss_out, sizeof(double), hipMemcpyDeviceToHost, h->stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+  if (e == hipSuccess) e = sync_all(h);
   if (e != hipSuccess) return hip_fail(e, "loss");
-  return CASGD_OK;
+  return check_status(h);
 }
 
 int casgd_debug_export(casgd_handle h, int what, void* dst, size_t bytes) {
@@ -311,14 +422,15 @@ int casgd_debug_export(casgd_handle h, int what, void* dst, size_t bytes) {
   if (h->last_s == 0) return fail(CASGD_EINVAL, "no outer step has run yet");
   const int s = h->last_s, b = h->last_b;
   const size_t sb = static_cast<size_t>(s) * b;
+  const StepBuffers& B = h->buf[h->last_buf];
   const void* src = nullptr;
   size_t need = 0;
   switch (what) {
-    case CASGD_EXPORT_IDX: src = h->idx; need = sb * sizeof(int32_t); break;
-    case CASGD_EXPORT_Y: src = h->Y; need = sb * h->ld * h->esize; break;
-    case CASGD_EXPORT_YB: src = h->yB; need = sb * sizeof(float); break;
+    case CASGD_EXPORT_IDX: src = B.idx; need = sb * sizeof(int32_t); break;
+    case CASGD_EXPORT_Y: src = B.Y; need = sb * h->ld * h->esize; break;
+    case CASGD_EXPORT_YB: src = B.yB; need = sb * sizeof(float); break;
     case CASGD_EXPORT_G:
-      src = h->G;
+      src = B.G;
       need = sizeof(float) * static_cast<size_t>(b) * b * s * (s - 1) / 2;
       break;
     case CASGD_EXPORT_V: src = h->v; need = sb * sizeof(float); break;
@@ -327,11 +439,10 @@ int casgd_debug_export(casgd_handle h, int what, void* dst, size_t bytes) {
     default: return fail(CASGD_EINVAL, "unknown export");
   }
   if (bytes != need) return fail(CASGD_EINVAL, "export size mismatch: need " + std::to_string(need));
-  if (need == 0) return CASGD_OK;
-  hipError_t e = hipMemcpyAsync(dst, src, need, hipMemcpyDeviceToHost, h->stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+  hipError_t e = sync_all(h);
+  if (e == hipSuccess && need > 0) e = hipMemcpy(dst, src, need, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "export");
-  return CASGD_OK;
+  return check_status(h);
 }
 
 int casgd_export_rows(casgd_handle h, int64_t row0, int64_t nrows, void* dst, size_t bytes) {
@@ -358,7 +469,7 @@ int casgd_get_timing(casgd_handle h, int kernel, double* total_ms, int64_t* laun
   if (!h) return fail(CASGD_EINVAL, "NULL handle");
   if (kernel < 0 || kernel >= CASGD_K_COUNT) return fail(CASGD_EINVAL, "unknown kernel id");
   if (!total_ms || !launches) return fail(CASGD_EINVAL, "NULL output");
-  hipError_t e = hipStreamSynchronize(h->stream);
+  hipError_t e = sync_all(h);
   if (e != hipSuccess) return hip_fail(e, "timing sync");
   for (int k = 0; k < CASGD_K_COUNT; ++k) {
     for (auto& p : h->pending[k]) {
@@ -377,7 +488,7 @@ int casgd_get_timing(casgd_handle h, int kernel, double* total_ms, int64_t* laun
     h->total_ms[kernel] = 0.0;
     h->launches[kernel] = 0;
   }
-  return CASGD_OK;
+  return check_status(h);
 }
 
 }  // extern "C"

@@ -7,6 +7,12 @@
 
 namespace casgd {
 
+// Native clang vectors for 16-byte loads and stores.  Arrays of these stay in
+// registers; arrays of HIP's struct vector types (uint4, float4) can end up in
+// scratch or LDS memory instead.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kLogistic = 0;
 constexpr int kSquared = 1;
 constexpr int kPoisson = 2;

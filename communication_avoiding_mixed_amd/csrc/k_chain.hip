@@ -1,0 +1,394 @@
+// The weight-dependent part of one CA-SGD outer iteration in a single launch:
+// margins, inner recurrence and weight update (Abstract of "Mixed-Precision
+// Communication-Avoiding SGD for Generalized Linear Models on GPUs": the inner
+// recurrence and the weight update run in high precision, here float32).
+//
+//   v   = Y w0
+//   z_j = v_j - c * sum_{t<j} G_{j,t} r_t,   r_j = l'(z_j, y_j),   c = eta / b
+//   w   = w0 - c * Y^T r
+//
+// Q workgroups split the b rows of every minibatch: workgroup q owns rows
+// i = q, q + Q, q + 2Q, ... of each minibatch, computes their margins, and at
+// inner step j the dot products of its rows of block-row j of G with the r
+// values of the earlier minibatches.  The new r values are exchanged through
+// 64-bit words that carry the launch's epoch tag in their upper half, so a
+// reader spins on the data itself (one one-way trip through the coherent
+// memory per inner step, no barriers, no separate flags).  Each value is
+// written to one mailbox per reading workgroup, so no memory location is
+// polled by more than one workgroup.  Every spin is
+// bounded: on expiry the kernel flags an error in `status` and returns.
+// After the last inner step every workgroup holds all of r and updates its
+// own slice of columns of w in a fixed summation order (no float atomics).
+#include "casgd_device.h"
+#include "casgd_internal.h"
+
+namespace casgd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr long kSpinLimit = 1L << 25;
+
+template <typename T>
+struct Elems;
+template <>
+struct Elems<uint16_t> {
+  static constexpr int E = 8;
+  __device__ static void widen(const u32x4& q, float (&f)[8]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
+      f[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+    }
+  }
+};
+template <>
+struct Elems<float> {
+  static constexpr int E = 4;
+  __device__ static void widen(const u32x4& q, float (&f)[4]) {
+    f[0] = __uint_as_float(q.x);
+    f[1] = __uint_as_float(q.y);
+    f[2] = __uint_as_float(q.z);
+    f[3] = __uint_as_float(q.w);
+  }
+};
+
+__device__ __forceinline__ uint64_t tagged(uint32_t epoch, float x) {
+  return (static_cast<uint64_t>(epoch) << 32) | __float_as_uint(x);
+}
+
+// LDS layout (floats): rs[sb] | vown[s * nown_max] | region, where region
+// holds this workgroup's rows of G (when a.preload) during the recurrence and
+// the update's reduction scratch afterwards.
+struct ChainLayout {
+  int64_t rs, vown, region, region_len, total;
+};
+
+__host__ __device__ inline ChainLayout chain_layout(int s, int b, int Q, bool preload) {
+  ChainLayout L;
+  const int64_t sb = static_cast<int64_t>(s) * b;
+  const int64_t nown_max = (b + Q - 1) / Q;
+  L.rs = 0;
+  L.vown = (sb + 3) & ~3LL;
+  L.region = L.vown + ((s * nown_max + 3) & ~3LL);
+  const int64_t gl = preload ? nown_max * b * (static_cast<int64_t>(s) * (s - 1) / 2) : 0;
+  L.region_len = gl > 2048 ? gl : 2048;
+  L.total = L.region + L.region_len;
+  return L;
+}
+
+template <typename T, int LOSS>
+__global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  constexpr int E = Elems<T>::E;
+  const int s = a.s, b = a.b, Q = a.Q;
+  const int sb = s * b;
+  const int q = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nown = (b - q + Q - 1) / Q;  // rows q, q+Q, ... below b
+  const ChainLayout L = chain_layout(s, b, Q, a.preload);
+  float* rs = sm + L.rs;      // r of all rows done so far
+  float* vown = sm + L.vown;  // margins of the own rows
+  float* gl = sm + L.region;  // own rows of G, then update scratch
+  __shared__ int abort_flag;
+  if (threadIdx.x == 0) abort_flag = 0;
+
+  const T* Y = static_cast<const T*>(a.Y);
+  const int64_t cpr = a.ld / E;  // 16-byte chunks per row
+  const bool w_vec = (reinterpret_cast<uintptr_t>(a.w) & 15) == 0;
+  const int64_t P = static_cast<int64_t>(b) * (static_cast<int64_t>(s) * (s - 1) / 2);
+
+  // ---- this workgroup's rows of every block-row of G into LDS, 16 loads in
+  // flight per lane.  Float4 f of own row t covers block-row j, columns
+  // 4k..4k+3 with f - t*P/4 = (b/4) j(j-1)/2 + k; its LDS slot is f itself.
+  if (a.preload) {
+    const int64_t P4 = P / 4;
+    const int64_t T4 = nown * P4;
+    const int b4 = b / 4;
+    const f32x4* G4 = reinterpret_cast<const f32x4*>(a.G);
+    f32x4* gl4 = reinterpret_cast<f32x4*>(gl);
+    for (int64_t f0 = threadIdx.x; f0 < T4; f0 += kThreads * 16) {
+      f32x4 tmp[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int64_t f = f0 + static_cast<int64_t>(kThreads) * u;
+        tmp[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (f < T4) {
+          const int t = static_cast<int>(f / P4);
+          const int64_t fr = f - t * P4;
+          const int64_t chunk = fr / b4;  // = j(j-1)/2 + k/b4
+          int j, kb;
+          block_of(static_cast<int>(chunk), j, kb);
+          const int64_t k4 = fr - static_cast<int64_t>(b4) * (static_cast<int64_t>(j) * (j - 1) / 2);
+          const int64_t i = q + static_cast<int64_t>(Q) * t;
+          tmp[u] = G4[(static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2) +
+                       i * j * b) / 4 + k4];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int64_t f = f0 + static_cast<int64_t>(kThreads) * u;
+        if (f < T4) gl4[f] = tmp[u];
+      }
+    }
+  }
+
+  // ---- margins of the own rows: each wave takes kRB rows at a time so that
+  // all of their loads are in flight together
+  constexpr int kRB = 4;
+  const int nrows_own = s * nown;
+  for (int p0 = wave * kRB; p0 < nrows_own; p0 += kWaves * kRB) {
+    float acc[kRB];
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) acc[r] = 0.f;
+    for (int64_t c0 = lane; c0 < cpr; c0 += 64 * 4) {
+      u32x4 qv[kRB][4];
+#pragma unroll
+      for (int r = 0; r < kRB; ++r) {
+        const int p = p0 + r;
+        const int j = p / nown;
+        const int t = p - j * nown;
+        const u32x4* yr = reinterpret_cast<const u32x4*>(
+            Y + (static_cast<int64_t>(j) * b + q + static_cast<int64_t>(Q) * t) * a.ld);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t c = c0 + 64 * u;
+          qv[r][u] = (p < nrows_own && c < cpr) ? yr[c] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = c0 + 64 * u;
+        if (c >= cpr) break;
+        const int64_t col0 = c * E;
+        float wv[E];
+        if (w_vec && col0 + E <= a.n) {
+          const f32x4* w4 = reinterpret_cast<const f32x4*>(a.w + col0);
+#pragma unroll
+          for (int h = 0; h < E / 4; ++h) {
+            const f32x4 ww = w4[h];
+            wv[4 * h + 0] = ww.x;
+            wv[4 * h + 1] = ww.y;
+            wv[4 * h + 2] = ww.z;
+            wv[4 * h + 3] = ww.w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) wv[e] = col0 + e < a.n ? a.w[col0 + e] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < kRB; ++r) {
+          float f[E];
+          Elems<T>::widen(qv[r][u], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[r] = fmaf(f[e], wv[e], acc[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) {
+      const float tot = group_sum<64>(acc[r]);
+      const int p = p0 + r;
+      if (lane == 0 && p < nrows_own) {
+        const int j = p / nown;
+        const int t = p - j * nown;
+        vown[p] = tot;
+        a.v[static_cast<int64_t>(j) * b + q + static_cast<int64_t>(Q) * t] = tot;
+      }
+    }
+  }
+  __syncthreads();  // vown and the G rows ready
+
+  // ---- inner recurrence.  Waves 1..3 compute and publish the own rows;
+  // wave 0 only polls for the step's r values, so its waits never queue
+  // behind another wave's memory traffic.
+  const bool vec = (b & 3) == 0;  // G rows are float4-aligned
+  for (int j = 0; j < s; ++j) {
+    const int jb = j * b;
+    if (wave > 0) {
+      const float* Gj = a.G + static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
+      for (int t = wave - 1; t < nown; t += kWaves - 1) {
+        const int i = q + Q * t;
+        float acc = 0.f;
+        if (a.preload) {
+          const f32x4* g4 = reinterpret_cast<const f32x4*>(gl + t * P + static_cast<int64_t>(b) * (static_cast<int64_t>(j) * (j - 1) / 2));
+          const f32x4* r4 = reinterpret_cast<const f32x4*>(rs);
+          for (int k4 = lane; k4 < (jb >> 2); k4 += 64) {
+            const f32x4 g = g4[k4];
+            const f32x4 rr = r4[k4];
+            acc = fmaf(g.x, rr.x, acc);
+            acc = fmaf(g.y, rr.y, acc);
+            acc = fmaf(g.z, rr.z, acc);
+            acc = fmaf(g.w, rr.w, acc);
+          }
+        } else if (vec) {
+          const f32x4* g4 = reinterpret_cast<const f32x4*>(Gj + static_cast<int64_t>(i) * jb);
+          const f32x4* r4 = reinterpret_cast<const f32x4*>(rs);
+          const int n4 = jb >> 2;
+          for (int k0 = lane; k0 < n4; k0 += 64 * 8) {
+            f32x4 g[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int k4 = k0 + 64 * u;
+              g[u] = k4 < n4 ? g4[k4] : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int k4 = k0 + 64 * u;
+              if (k4 < n4) {
+                const f32x4 rr = r4[k4];
+                acc = fmaf(g[u].x, rr.x, acc);
+                acc = fmaf(g[u].y, rr.y, acc);
+                acc = fmaf(g[u].z, rr.z, acc);
+                acc = fmaf(g[u].w, rr.w, acc);
+              }
+            }
+          }
+        } else {
+          const float* grow = Gj + static_cast<int64_t>(i) * jb;
+          for (int k = lane; k < jb; k += 64) acc = fmaf(grow[k], rs[k], acc);
+        }
+        acc = group_sum<64>(acc);  // every lane holds the sum
+        const int64_t row = jb + i;
+        const float zz = vown[j * nown + t] - a.c * acc;
+        const float rv = loss_deriv<LOSS>(zz, a.yB[row]);
+        const uint64_t word = tagged(a.epoch, rv);
+        // one copy per reader: each workgroup polls only its own mailbox
+        for (int dst = lane; dst < Q; dst += 64)
+          __hip_atomic_store(&a.xbuf[static_cast<int64_t>(dst) * sb + row], word, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) {
+          a.z[row] = zz;
+          a.r[row] = rv;
+        }
+      }
+    } else {
+      // collect r_j of every row from this workgroup's mailbox
+      const unsigned long long* mbox = a.xbuf + static_cast<int64_t>(q) * sb;
+      for (int k = lane; k < b; k += 64) {
+        uint64_t x = 0;
+        long it = 0;
+        while (true) {
+          x = __hip_atomic_load(&mbox[jb + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (static_cast<uint32_t>(x >> 32) == a.epoch) break;
+          if (++it > kSpinLimit) {
+            abort_flag = 1;
+            atomicOr(a.status, 1);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        rs[jb + k] = __uint_as_float(static_cast<uint32_t>(x));
+      }
+    }
+    __syncthreads();
+    if (abort_flag) return;
+  }
+
+  // ---- update: w[col] -= c * sum_rows Y[row][col] r[row] on this workgroup's columns
+  float* red = gl;  // the G rows are no longer needed
+  const int64_t per = (cpr + Q - 1) / Q;
+  const int64_t ch0 = static_cast<int64_t>(q) * per;
+  const int64_t ch1 = ch0 + per < cpr ? ch0 + per : cpr;
+  int cw = 1;
+  while (cw < per && cw < 64) cw <<= 1;
+  const int rgn = kThreads / cw;
+  const int cl = threadIdx.x % cw;
+  const int rg = threadIdx.x / cw;
+  const u32x4* Y4 = reinterpret_cast<const u32x4*>(Y);
+  for (int64_t cb = ch0; cb < ch1; cb += cw) {
+    const int64_t ch = cb + cl;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    if (ch < ch1) {
+      int row = rg;
+      for (; row + 15 * rgn < sb; row += 16 * rgn) {
+        u32x4 qv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) qv[u] = Y4[static_cast<int64_t>(row + u * rgn) * cpr + ch];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          float f[E];
+          Elems<T>::widen(qv[u], f);
+          const float rr = rs[row + u * rgn];
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] = fmaf(f[e], rr, acc[e]);
+        }
+      }
+      for (; row < sb; row += rgn) {
+        float f[E];
+        Elems<T>::widen(Y4[static_cast<int64_t>(row) * cpr + ch], f);
+        const float rr = rs[row];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(f[e], rr, acc[e]);
+      }
+    }
+    __syncthreads();  // red is reused across column blocks
+#pragma unroll
+    for (int e = 0; e < E; ++e) red[rg * (cw * E) + cl * E + e] = acc[e];
+    __syncthreads();
+    for (int o = threadIdx.x; o < cw * E; o += kThreads) {
+      float sum = 0.f;
+      for (int g = 0; g < rgn; ++g) sum += red[g * (cw * E) + o];
+      const int64_t chunk = cb + o / E;
+      const int64_t col = chunk * E + o % E;
+      if (chunk < ch1 && col < a.n) a.w[col] = a.w[col] - a.c * sum;
+    }
+  }
+}
+
+template <typename T, int LOSS>
+hipError_t chain_t(const ChainArgs& a, size_t lds, hipStream_t st) {
+  // dynamic LDS above the default 64 KB cap must be requested per kernel
+  static size_t granted = 64 * 1024;
+  if (lds > granted) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chain_kernel<T, LOSS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    granted = lds;
+  }
+  chain_kernel<T, LOSS><<<a.Q, kThreads, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Whole-CU LDS per workgroup keeps other kernels' workgroups off the CUs that
+// run the recurrence, whose inner steps are latency-bound.
+constexpr size_t kLdsBudget = 160 * 1024 - 256;
+constexpr size_t kLdsReserve = 136 * 1024;
+
+bool chain_preload(int s, int b, int Q) {
+  if ((b & 3) != 0) return false;
+  return static_cast<size_t>(chain_layout(s, b, Q, true).total) * sizeof(float) <= kLdsBudget;
+}
+
+size_t chain_lds_bytes(int s, int b, int Q) {
+  const size_t need = static_cast<size_t>(chain_layout(s, b, Q, chain_preload(s, b, Q)).total) * sizeof(float);
+  return need > kLdsReserve ? need : kLdsReserve;
+}
+
+int chain_workgroups(int s, int b) {
+  (void)s;
+  return b < kChainMaxWorkgroups ? b : kChainMaxWorkgroups;
+}
+
+hipError_t launch_chain(int storage, int loss, const ChainArgs& a_in, hipStream_t st) {
+  ChainArgs a = a_in;
+  a.preload = chain_preload(a.s, a.b, a.Q) ? 1 : 0;
+  const size_t lds = chain_lds_bytes(a.s, a.b, a.Q);
+  if (storage == kStoreBF16) {
+    if (loss == kLogistic) return chain_t<uint16_t, kLogistic>(a, lds, st);
+    if (loss == kSquared) return chain_t<uint16_t, kSquared>(a, lds, st);
+    return chain_t<uint16_t, kPoisson>(a, lds, st);
+  }
+  if (loss == kLogistic) return chain_t<float, kLogistic>(a, lds, st);
+  if (loss == kSquared) return chain_t<float, kSquared>(a, lds, st);
+  return chain_t<float, kPoisson>(a, lds, st);
+}
+
+}  // namespace casgd

@@ -21,15 +21,17 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 64;  // output tile edge; 4 waves of 32 x 32
 
-// One 64 x 64 output tile per workgroup of 256 lanes.  blockIdx.x enumerates
-// (block (j,t), tile row, tile col); blockIdx.y is the problem (outer step).
-// Rows past the block edge (b not a multiple of 64) load as zeros and are not
-// stored.  K is walked in BK-wide stages, double-buffered through LDS.
-template <int BK>
+// One 64 x 64 output tile per workgroup of 256 lanes; blockIdx.x enumerates
+// (block (j,t), tile row, tile col).  Rows past the block edge (b not a
+// multiple of 64) load as zeros and are not stored.  K is walked in BK-wide
+// stages: each stage's global loads are issued D stages before it is used
+// (a ring of D register sets per lane), then the stage is copied into one of
+// two LDS buffers and consumed by the MFMAs.  Keeping D stages in flight
+// hides the memory latency that a one-stage prefetch leaves exposed.
+template <int BK, int D>
 __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restrict__ Y,
-                                                        int64_t ld, int s, int b, int tps,
-                                                        float* __restrict__ G, int64_t y_stride,
-                                                        int64_t g_stride) {
+                                                        int64_t ld, int b, int tps,
+                                                        float* __restrict__ G) {
   constexpr int CPR = BK / 8;          // 16-byte chunks per tile row per stage
   constexpr int RPP = 256 / CPR;       // tile rows loaded per pass
   constexpr int PASSES = kTile / RPP;  // passes per operand per stage
@@ -39,17 +41,15 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restri
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * LW];
 
   const int nt2 = tps * tps;
-  const int p = blockIdx.x / nt2;
-  const int rem = blockIdx.x - p * nt2;
+  const int tile = blockIdx.x;
+  const int p = tile / nt2;
+  const int rem = tile - p * nt2;
   const int ti = rem / tps;
   const int tj = rem - ti * tps;
   int j, t;
   block_of(p, j, t);
-  (void)s;
 
-  const uint16_t* Yp = Y + static_cast<int64_t>(blockIdx.y) * y_stride;
-  float* Gj = G + static_cast<int64_t>(blockIdx.y) * g_stride +
-              static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
+  float* Gj = G + static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
   const int64_t ldg = static_cast<int64_t>(j) * b;
   const int a0 = ti * kTile;  // first row of the A tile inside block-row j
   const int b0 = tj * kTile;  // first row of the B tile inside block-row t
@@ -64,25 +64,19 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restri
     const int r = lrow + q * RPP;
     aok[q] = a0 + r < b;
     bok[q] = b0 + r < b;
-    aptr[q] = Yp + (static_cast<int64_t>(j) * b + a0 + (aok[q] ? r : 0)) * ld + lchunk * 8;
-    bptr[q] = Yp + (static_cast<int64_t>(t) * b + b0 + (bok[q] ? r : 0)) * ld + lchunk * 8;
+    aptr[q] = Y + (static_cast<int64_t>(j) * b + a0 + (aok[q] ? r : 0)) * ld + lchunk * 8;
+    bptr[q] = Y + (static_cast<int64_t>(t) * b + b0 + (bok[q] ? r : 0)) * ld + lchunk * 8;
   }
 
-  uint4 ra[PASSES], rb[PASSES];
-  auto load_stage = [&](int64_t k0) {
+  u32x4 ra[D][PASSES], rb[D][PASSES];
+  const int64_t nstage = (ld + BK - 1) / BK;
+  auto load_stage = [&](int slot, int64_t st) {
+    const int64_t k0 = st * BK;
     const bool kin = k0 + lchunk * 8 < ld;  // last stage may be half-width
 #pragma unroll
     for (int q = 0; q < PASSES; ++q) {
-      ra[q] = (aok[q] && kin) ? *reinterpret_cast<const uint4*>(aptr[q] + k0) : make_uint4(0, 0, 0, 0);
-      rb[q] = (bok[q] && kin) ? *reinterpret_cast<const uint4*>(bptr[q] + k0) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < PASSES; ++q) {
-      const int r = lrow + q * RPP;
-      *reinterpret_cast<uint4*>(&As[buf][r * LW + lchunk * 8]) = ra[q];
-      *reinterpret_cast<uint4*>(&Bs[buf][r * LW + lchunk * 8]) = rb[q];
+      ra[slot][q] = (aok[q] && kin) ? *reinterpret_cast<const u32x4*>(aptr[q] + k0) : u32x4{0u, 0u, 0u, 0u};
+      rb[slot][q] = (bok[q] && kin) ? *reinterpret_cast<const u32x4*>(bptr[q] + k0) : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -97,22 +91,30 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restri
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 
-  const int64_t nstage = (ld + BK - 1) / BK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int64_t st = 0; st < nstage; ++st) {
-    const int buf = static_cast<int>(st & 1);
-    if (st + 1 < nstage) load_stage((st + 1) * BK);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&As[buf][arow * LW + kk * 16 + kofs]);
-      const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][brow * LW + kk * 16 + kofs]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
-    }
-    if (st + 1 < nstage) {
-      store_stage(buf ^ 1);
+  for (int d = 0; d < D; ++d)
+    if (d < nstage) load_stage(d, d);
+
+  for (int64_t st0 = 0; st0 < nstage; st0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int64_t cur = st0 + d;
+      if (cur >= nstage) break;
+      const int buf = static_cast<int>(cur & 1);
+#pragma unroll
+      for (int q = 0; q < PASSES; ++q) {
+        const int r = lrow + q * RPP;
+        *reinterpret_cast<u32x4*>(&As[buf][r * LW + lchunk * 8]) = ra[d][q];
+        *reinterpret_cast<u32x4*>(&Bs[buf][r * LW + lchunk * 8]) = rb[d][q];
+      }
       __syncthreads();
+      if (cur + D < nstage) load_stage(d, cur + D);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&As[buf][arow * LW + kk * 16 + kofs]);
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][brow * LW + kk * 16 + kofs]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+      }
     }
   }
 
@@ -132,9 +134,7 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restri
 // float32 storage: the same tiles on the vector ALUs (each lane a 4 x 4
 // register block), used when the data are kept in float32.
 __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__ Y, int64_t ld,
-                                                       int s, int b, int tps,
-                                                       float* __restrict__ G, int64_t y_stride,
-                                                       int64_t g_stride) {
+                                                       int b, int tps, float* __restrict__ G) {
   constexpr int BK = 16;
   __shared__ float As[BK][kTile + 4];
   __shared__ float Bs[BK][kTile + 4];
@@ -145,10 +145,8 @@ __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__
   const int tj = rem - ti * tps;
   int j, t;
   block_of(p, j, t);
-  (void)s;
-  const float* Yp = Y + static_cast<int64_t>(blockIdx.y) * y_stride;
-  float* Gj = G + static_cast<int64_t>(blockIdx.y) * g_stride +
-              static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
+  const float* Yp = Y;
+  float* Gj = G + static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
   const int64_t ldg = static_cast<int64_t>(j) * b;
   const int a0 = ti * kTile, b0 = tj * kTile;
 
@@ -201,22 +199,27 @@ __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_gram(int storage, const void* Y, int64_t ld, int s, int b, float* G, int nprob,
-                       int64_t y_stride, int64_t g_stride, hipStream_t st) {
-  const int nblocks = s * (s - 1) / 2;
-  if (nblocks == 0 || nprob == 0) return hipSuccess;
+GramPlan gram_plan(int storage, int s, int b, int64_t ld) {
+  (void)storage;
+  (void)ld;
+  GramPlan p;
   const int tps = (b + kTile - 1) / kTile;
-  const dim3 grid(static_cast<unsigned>(nblocks * tps * tps), static_cast<unsigned>(nprob));
+  p.tiles = s * (s - 1) / 2 * tps * tps;
+  return p;
+}
+
+hipError_t launch_gram(int storage, const void* Y, int64_t ld, int s, int b, float* G,
+                       const GramPlan& plan, hipStream_t st) {
+  (void)s;
+  if (plan.tiles == 0) return hipSuccess;
+  const int tps = (b + kTile - 1) / kTile;
   if (storage == kStoreBF16) {
-    if (ld % 64 == 0 || ld > 32)
-      gram_bf16_kernel<64><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(Y), ld, s, b, tps, G,
-                                                  y_stride, g_stride);
+    if (ld > 32)
+      gram_bf16_kernel<64, 8><<<plan.tiles, 256, 0, st>>>(static_cast<const uint16_t*>(Y), ld, b, tps, G);
     else
-      gram_bf16_kernel<32><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(Y), ld, s, b, tps, G,
-                                                  y_stride, g_stride);
+      gram_bf16_kernel<32, 1><<<plan.tiles, 256, 0, st>>>(static_cast<const uint16_t*>(Y), ld, b, tps, G);
   } else {
-    gram_f32_kernel<<<grid, 256, 0, st>>>(static_cast<const float*>(Y), ld, s, b, tps, G, y_stride,
-                                          g_stride);
+    gram_f32_kernel<<<plan.tiles, 256, 0, st>>>(static_cast<const float*>(Y), ld, b, tps, G);
   }
   return hipGetLastError();
 }

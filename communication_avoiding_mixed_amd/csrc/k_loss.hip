@@ -14,7 +14,7 @@ struct Widen;
 template <>
 struct Widen<uint16_t> {
   static constexpr int kElems = 8;
-  __device__ static void run(const uint4& q, float (&f)[8]) {
+  __device__ static void run(const u32x4& q, float (&f)[8]) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -26,7 +26,7 @@ struct Widen<uint16_t> {
 template <>
 struct Widen<float> {
   static constexpr int kElems = 4;
-  __device__ static void run(const uint4& q, float (&f)[4]) {
+  __device__ static void run(const u32x4& q, float (&f)[4]) {
     f[0] = __uint_as_float(q.x);
     f[1] = __uint_as_float(q.y);
     f[2] = __uint_as_float(q.z);
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void loss_kernel(const T* __restrict__ Xs,
   double acc = 0.0;
   for (int64_t row = static_cast<int64_t>(blockIdx.x) * (256 / GS) + threadIdx.x / GS; row < m;
        row += groups) {
-    const uint4* xr = reinterpret_cast<const uint4*>(Xs + row * ld);
+    const u32x4* xr = reinterpret_cast<const u32x4*>(Xs + row * ld);
     float d = 0.f;
     for (int64_t c = lane; c < cpr; c += GS) {
       float f[E];

@@ -65,11 +65,10 @@ enum casgd_export_what {
 
 /* Timers kept when timing is on (casgd_set_timing). */
 enum casgd_kernel_id {
-  CASGD_K_GATHER = 0, /* sample + gather + margins        */
-  CASGD_K_GRAM = 1,   /* strictly-lower Gram on MFMA      */
-  CASGD_K_RECUR = 2,  /* inner recurrence                 */
-  CASGD_K_UPDATE = 3, /* transposed-GEMV weight update    */
-  CASGD_K_COUNT = 4
+  CASGD_K_GATHER = 0, /* sample + gather of the s*b rows                        */
+  CASGD_K_GRAM = 1,   /* strictly-lower Gram on bf16 MFMA                       */
+  CASGD_K_CHAIN = 2,  /* margins + inner recurrence + weight update (one launch) */
+  CASGD_K_COUNT = 3
 };
 
 /*
@@ -90,7 +89,7 @@ enum casgd_kernel_id {
 casgd_handle casgd_create(const float* X, const float* y, int64_t m, int64_t n,
                           int loss, int storage);
 
-/* Free everything the handle owns.  NULL is allowed.  Synchronises its stream. */
+/* Free everything the handle owns.  NULL is allowed.  Synchronises its streams. */
 void casgd_destroy(casgd_handle h);
 
 /* Queue later work on hip_stream (a hipStream_t; NULL selects the null stream). */
@@ -106,6 +105,9 @@ int casgd_set_stream(casgd_handle h, void* hip_stream);
  *   w      device, float32 [n]; read as w0, overwritten with the new weights
  *          in stream order; must not alias handle memory
  * Asynchronous.  Workspace grows on the first call with a larger s*b.
+ * Sampling, gathering and the Gram run on a stream the handle owns, ordered
+ * before the weight-dependent kernel on the handle's stream; the next call's
+ * sampling, gathering and Gram may overlap this call's recurrence.
  */
 int casgd_outer_step(casgd_handle h, int s, int b, float eta, uint64_t seed, float* w);
 
@@ -133,6 +135,8 @@ uint64_t casgd_step_seed(uint64_t base_seed, uint64_t k);
  * Mean loss over every stored row, f(w) = (1/m) sum_i l(x_i . w, y_i): float32
  * dot products, float64 loss terms and sums (the Abstract compares methods by
  * this loss).  w: device float32 [n].  out: host double.  Synchronises.
+ * Also reports CASGD_EHIP if an earlier outer step's exchange between
+ * workgroups timed out (a wait is bounded instead of hanging).
  */
 int casgd_loss(casgd_handle h, const float* w, double* out);
 
