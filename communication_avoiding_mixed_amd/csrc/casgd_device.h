@@ -78,13 +78,39 @@ __device__ __forceinline__ double loss_value(double z, double y) {
   }
 }
 
+// Cross-lane move inside rows of 16 lanes (DPP).  CTRL: 0xB1 / 0x4E swap
+// neighbours 1 / 2 apart in each quad, 0x124 / 0x128 rotate a row by 4 / 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront, the same value in every lane.  Rows
+// of 16 are summed with DPP moves, then the four row sums are read out and
+// added in a fixed order, so the result does not depend on timing.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_move<0xB1>(v);
+  v += dpp_move<0x4E>(v);
+  v += dpp_move<0x124>(v);
+  v += dpp_move<0x128>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
 // Reduction over the `width` lanes of an aligned lane group (width a power of
 // two up to the 64-lane wavefront).
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float x) {
+  if constexpr (WIDTH == 64) {
+    return wave_sum(x);
+  } else {
 #pragma unroll
-  for (int o = WIDTH / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, WIDTH);
-  return x;
+    for (int o = WIDTH / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, WIDTH);
+    return x;
+  }
 }
 
 template <int WIDTH>

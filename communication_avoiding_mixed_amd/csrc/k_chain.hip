@@ -58,11 +58,12 @@ __device__ __forceinline__ uint64_t tagged(uint32_t epoch, float x) {
   return (static_cast<uint64_t>(epoch) << 32) | __float_as_uint(x);
 }
 
-// LDS layout (floats): rs[sb] | vown[s * nown_max] | region, where region
+// LDS layout (floats): rs[sb] | vown[s * nown_max] | yown[s * nown_max] |
+// region, where region
 // holds this workgroup's rows of G (when a.preload) during the recurrence and
 // the update's reduction scratch afterwards.
 struct ChainLayout {
-  int64_t rs, vown, region, region_len, total;
+  int64_t rs, vown, yown, region, region_len, total;
 };
 
 __host__ __device__ inline ChainLayout chain_layout(int s, int b, int Q, bool preload) {
@@ -71,7 +72,8 @@ __host__ __device__ inline ChainLayout chain_layout(int s, int b, int Q, bool pr
   const int64_t nown_max = (b + Q - 1) / Q;
   L.rs = 0;
   L.vown = (sb + 3) & ~3LL;
-  L.region = L.vown + ((s * nown_max + 3) & ~3LL);
+  L.yown = L.vown + ((s * nown_max + 3) & ~3LL);
+  L.region = L.yown + ((s * nown_max + 3) & ~3LL);
   const int64_t gl = preload ? nown_max * b * (static_cast<int64_t>(s) * (s - 1) / 2) : 0;
   L.region_len = gl > 2048 ? gl : 2048;
   L.total = L.region + L.region_len;
@@ -91,6 +93,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   const ChainLayout L = chain_layout(s, b, Q, a.preload);
   float* rs = sm + L.rs;      // r of all rows done so far
   float* vown = sm + L.vown;  // margins of the own rows
+  float* yown = sm + L.yown;  // labels / targets of the own rows
   float* gl = sm + L.region;  // own rows of G, then update scratch
   __shared__ int abort_flag;
   if (threadIdx.x == 0) abort_flag = 0;
@@ -194,8 +197,10 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
       if (lane == 0 && p < nrows_own) {
         const int j = p / nown;
         const int t = p - j * nown;
+        const int64_t row = static_cast<int64_t>(j) * b + q + static_cast<int64_t>(Q) * t;
         vown[p] = tot;
-        a.v[static_cast<int64_t>(j) * b + q + static_cast<int64_t>(Q) * t] = tot;
+        yown[p] = a.yB[row];
+        a.v[row] = tot;
       }
     }
   }
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
         acc = group_sum<64>(acc);  // every lane holds the sum
         const int64_t row = jb + i;
         const float zz = vown[j * nown + t] - a.c * acc;
-        const float rv = loss_deriv<LOSS>(zz, a.yB[row]);
+        const float rv = loss_deriv<LOSS>(zz, yown[j * nown + t]);
         const uint64_t word = tagged(a.epoch, rv);
         // one copy per reader: each workgroup polls only its own mailbox
         for (int dst = lane; dst < Q; dst += 64)
