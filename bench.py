@@ -73,6 +73,20 @@ def cpu_baseline(X, y, wl, budget_s: float):
     }
 
 
+def copy_calibration(nbytes: int):
+    """One plain device copy of nbytes (reads nbytes, writes nbytes), timed."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "seconds": el}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,7 +95,13 @@ def main():
     ap.add_argument("--workload", default="epsilon")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES between two device buffers (a plain copy kernel of "
+                         "known traffic, to scale the HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU "
               "column-partitioned path is not built", file=sys.stderr)

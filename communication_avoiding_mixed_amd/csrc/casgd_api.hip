@@ -70,6 +70,8 @@ struct casgd_ctx {
   float* r = nullptr;
   int32_t* idx_user = nullptr;
   unsigned long long* xbuf = nullptr;
+  int* order = nullptr;          // Gram workgroup -> tile table for (order_s, order_b)
+  int order_cap = 0, order_s = 0, order_b = 0;
   int* status = nullptr;
   double* loss_partial = nullptr;
   double* loss_out = nullptr;
@@ -106,6 +108,8 @@ void free_workspace(casgd_ctx* h) {
   release(h->r);
   release(h->idx_user);
   release(h->xbuf);
+  release(h->order);
+  h->order_cap = h->order_s = h->order_b = 0;
   h->cap_sb = 0;
   h->cap_g = 0;
 }
@@ -156,6 +160,28 @@ int ensure_workspace(casgd_ctx* h, int s, int b) {
   return CASGD_OK;
 }
 
+// The Gram's XCD-grouped tile order for shape (s, b), rebuilt when the shape changes.
+int ensure_order(casgd_ctx* h, int s, int b) {
+  if (h->order && h->order_s == s && h->order_b == b) return CASGD_OK;
+  const std::vector<int> order = casgd::gram_order(s, b);
+  hipError_t e = sync_all(h);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  if (static_cast<int>(order.size()) > h->order_cap) {
+    release(h->order);
+    h->order_cap = 0;
+    if (!grab(h->order, sizeof(int) * (order.size() > 0 ? order.size() : 1)))
+      return fail(CASGD_ENOMEM, "device allocation of the Gram tile order failed");
+    h->order_cap = static_cast<int>(order.size());
+  }
+  if (!order.empty()) {
+    e = hipMemcpy(h->order, order.data(), sizeof(int) * order.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "uploading the Gram tile order");
+  }
+  h->order_s = s;
+  h->order_b = b;
+  return CASGD_OK;
+}
+
 EventPair take_pair(casgd_ctx* h) {
   if (!h->pool.empty()) {
     EventPair p = h->pool.back();
@@ -168,14 +194,13 @@ EventPair take_pair(casgd_ctx* h) {
   return p;
 }
 
-// Launch `fn` on `st`, bracketed by events when timing is on.
+// Call fn(timer): with timing on, the timer's events are stamped by the
+// kernel's own dispatch (start and end of that kernel).
 template <typename Fn>
-hipError_t timed(casgd_ctx* h, int kernel, hipStream_t st, Fn&& fn) {
-  if (!h->timing) return fn();
+hipError_t timed(casgd_ctx* h, int kernel, Fn&& fn) {
+  if (!h->timing) return fn(casgd::LaunchTimer{});
   EventPair p = take_pair(h);
-  (void)hipEventRecord(p.start, st);
-  hipError_t e = fn();
-  (void)hipEventRecord(p.stop, st);
+  hipError_t e = fn(casgd::LaunchTimer{p.start, p.stop});
   h->pending[kernel].push_back(p);
   return e;
 }
@@ -205,6 +230,8 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
               float* w) {
   int rc = ensure_workspace(h, s, b);
   if (rc != CASGD_OK) return rc;
+  rc = ensure_order(h, s, b);
+  if (rc != CASGD_OK) return rc;
   const int sb = s * b;
   const float c = eta / static_cast<float>(b);
   const int k = h->next_buf;
@@ -214,14 +241,14 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   // weight-independent part, on the prep stream
   e = hipStreamWaitEvent(h->prep, h->ev_chain[k], 0);
   if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-  e = timed(h, CASGD_K_GATHER, h->prep, [&] {
+  e = timed(h, CASGD_K_GATHER, [&](const casgd::LaunchTimer& tm) {
     return casgd::launch_gather(h->storage, h->Xs, h->y, h->m, h->ld, sb, seed, idx_in, B.idx,
-                                B.Y, B.yB, h->prep);
+                                B.Y, B.yB, h->prep, tm);
   });
   if (e != hipSuccess) return hip_fail(e, "gather launch");
   const casgd::GramPlan plan = casgd::gram_plan(h->storage, s, b, h->ld);
-  e = timed(h, CASGD_K_GRAM, h->prep, [&] {
-    return casgd::launch_gram(h->storage, B.Y, h->ld, s, b, B.G, plan, h->prep);
+  e = timed(h, CASGD_K_GRAM, [&](const casgd::LaunchTimer& tm) {
+    return casgd::launch_gram(h->storage, B.Y, h->ld, s, b, B.G, plan, h->order, h->prep, tm);
   });
   if (e != hipSuccess) return hip_fail(e, "gram launch");
   e = hipEventRecord(h->ev_prep[k], h->prep);
@@ -247,8 +274,9 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   a.xbuf = h->xbuf;
   a.epoch = ++h->epoch == 0 ? ++h->epoch : h->epoch;
   a.status = h->status;
-  e = timed(h, CASGD_K_CHAIN, h->stream,
-            [&] { return casgd::launch_chain(h->storage, h->loss, a, h->stream); });
+  e = timed(h, CASGD_K_CHAIN, [&](const casgd::LaunchTimer& tm) {
+    return casgd::launch_chain(h->storage, h->loss, a, h->stream, tm);
+  });
   if (e != hipSuccess) return hip_fail(e, "recurrence launch");
   e = hipEventRecord(h->ev_chain[k], h->stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");

@@ -3,11 +3,32 @@
 // layer before any of these is called.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace casgd {
+
+// Optional pair of HIP events stamped by the kernel dispatch itself (start and
+// end of the kernel), so a timed launch measures the kernel and not the queue.
+struct LaunchTimer {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename... Params, typename... Args>
+hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds,
+                         hipStream_t stream, const LaunchTimer& tm, Args... args) {
+  if (tm.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), stream, tm.start, tm.stop,
+                          0u, static_cast<Params>(args)...);
+  else
+    kernel<<<grid, block, lds, stream>>>(static_cast<Params>(args)...);
+  return hipGetLastError();
+}
 
 constexpr int kStoreBF16 = 0;
 constexpr int kStoreF32 = 1;
@@ -19,16 +40,22 @@ hipError_t launch_store(int storage, const float* X, void* Xs, int64_t m, int64_
 // Sample (or take idx_in), gather rows into Y and labels into yB.
 hipError_t launch_gather(int storage, const void* Xs, const float* y, int64_t m, int64_t ld,
                          int sb, uint64_t seed, const int32_t* idx_in, int32_t* idx_out,
-                         void* Y, float* yB, hipStream_t stream);
+                         void* Y, float* yB, hipStream_t stream, const LaunchTimer& tm = {});
 
 // Strictly-lower block triangle of Y Y^T in block-row layout, one 64 x 64
 // output tile per workgroup.
+// `order` (device, plan.slots ints) maps workgroups to tiles so that tiles
+// sharing rows of Y run on the same XCD; build it with gram_order.
+constexpr int kXcds = 8;
 struct GramPlan {
   int tiles = 0;  // 64 x 64 output tiles
+  int slots = 0;  // workgroups launched: tiles rounded up to a multiple of kXcds
 };
 GramPlan gram_plan(int storage, int s, int b, int64_t ld);
+std::vector<int> gram_order(int s, int b);
 hipError_t launch_gram(int storage, const void* Y, int64_t ld, int s, int b, float* G,
-                       const GramPlan& plan, hipStream_t stream);
+                       const GramPlan& plan, const int* order, hipStream_t stream,
+                       const LaunchTimer& tm = {});
 
 // Margins, inner recurrence and update in one launch of Q workgroups.
 struct ChainArgs {
@@ -51,7 +78,8 @@ struct ChainArgs {
 size_t chain_lds_bytes(int s, int b, int Q);
 int chain_workgroups(int s, int b);
 constexpr int kChainMaxWorkgroups = 64;
-hipError_t launch_chain(int storage, int loss, const ChainArgs& a, hipStream_t stream);
+hipError_t launch_chain(int storage, int loss, const ChainArgs& a, hipStream_t stream,
+                        const LaunchTimer& tm = {});
 
 // Mean loss over all m stored rows into out_dev (one double); partial must
 // hold kLossBlocks doubles.

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
 }
 
 template <typename T, int LOSS>
-hipError_t chain_t(const ChainArgs& a, size_t lds, hipStream_t st) {
+hipError_t chain_t(const ChainArgs& a, size_t lds, hipStream_t st, const LaunchTimer& tm) {
   // dynamic LDS above the default 64 KB cap must be requested per kernel
   static size_t granted = 64 * 1024;
   if (lds > granted) {
@@ -356,8 +356,7 @@ hipError_t chain_t(const ChainArgs& a, size_t lds, hipStream_t st) {
     if (e != hipSuccess) return e;
     granted = lds;
   }
-  chain_kernel<T, LOSS><<<a.Q, kThreads, lds, st>>>(a);
-  return hipGetLastError();
+  return launch_kernel(chain_kernel<T, LOSS>, dim3(a.Q), dim3(kThreads), lds, st, tm, a);
 }
 
 }  // namespace
@@ -382,18 +381,19 @@ int chain_workgroups(int s, int b) {
   return b < kChainMaxWorkgroups ? b : kChainMaxWorkgroups;
 }
 
-hipError_t launch_chain(int storage, int loss, const ChainArgs& a_in, hipStream_t st) {
+hipError_t launch_chain(int storage, int loss, const ChainArgs& a_in, hipStream_t st,
+                        const LaunchTimer& tm) {
   ChainArgs a = a_in;
   a.preload = chain_preload(a.s, a.b, a.Q) ? 1 : 0;
   const size_t lds = chain_lds_bytes(a.s, a.b, a.Q);
   if (storage == kStoreBF16) {
-    if (loss == kLogistic) return chain_t<uint16_t, kLogistic>(a, lds, st);
-    if (loss == kSquared) return chain_t<uint16_t, kSquared>(a, lds, st);
-    return chain_t<uint16_t, kPoisson>(a, lds, st);
+    if (loss == kLogistic) return chain_t<uint16_t, kLogistic>(a, lds, st, tm);
+    if (loss == kSquared) return chain_t<uint16_t, kSquared>(a, lds, st, tm);
+    return chain_t<uint16_t, kPoisson>(a, lds, st, tm);
   }
-  if (loss == kLogistic) return chain_t<float, kLogistic>(a, lds, st);
-  if (loss == kSquared) return chain_t<float, kSquared>(a, lds, st);
-  return chain_t<float, kPoisson>(a, lds, st);
+  if (loss == kLogistic) return chain_t<float, kLogistic>(a, lds, st, tm);
+  if (loss == kSquared) return chain_t<float, kSquared>(a, lds, st, tm);
+  return chain_t<float, kPoisson>(a, lds, st, tm);
 }
 
 }  // namespace casgd

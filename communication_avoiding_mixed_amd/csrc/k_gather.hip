@@ -95,12 +95,13 @@ __global__ __launch_bounds__(256) void gather_kernel(
 
 template <int GS>
 hipError_t gather_t(const void* Xs, const float* y, int64_t m, int64_t cpr, int sb, uint64_t seed,
-                    const int32_t* idx_in, int32_t* idx_out, void* Y, float* yB, hipStream_t st) {
+                    const int32_t* idx_in, int32_t* idx_out, void* Y, float* yB, hipStream_t st,
+                    const LaunchTimer& tm) {
   const int rows_per_block = 256 / GS;
   const int grid = (sb + rows_per_block - 1) / rows_per_block;
-  gather_kernel<GS><<<grid, 256, 0, st>>>(static_cast<const u32x4*>(Xs), y, m, cpr, sb, seed,
-                                          idx_in, idx_out, static_cast<u32x4*>(Y), yB);
-  return hipGetLastError();
+  return launch_kernel(gather_kernel<GS>, dim3(grid), dim3(256), 0, st, tm,
+                       static_cast<const u32x4*>(Xs), y, m, cpr, sb, seed, idx_in, idx_out,
+                       static_cast<u32x4*>(Y), yB);
 }
 
 }  // namespace
@@ -119,13 +120,13 @@ hipError_t launch_store(int storage, const float* X, void* Xs, int64_t m, int64_
 
 hipError_t launch_gather(int storage, const void* Xs, const float* y, int64_t m, int64_t ld,
                          int sb, uint64_t seed, const int32_t* idx_in, int32_t* idx_out, void* Y,
-                         float* yB, hipStream_t st) {
+                         float* yB, hipStream_t st, const LaunchTimer& tm) {
   const int64_t cpr = ld / (storage == kStoreBF16 ? 8 : 4);  // 16-byte chunks per row
-  if (cpr >= 64) return gather_t<64>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, st);
-  if (cpr >= 32) return gather_t<32>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, st);
-  if (cpr >= 16) return gather_t<16>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, st);
-  if (cpr >= 8) return gather_t<8>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, st);
-  return gather_t<4>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, st);
+  if (cpr >= 64) return gather_t<64>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, st, tm);
+  if (cpr >= 32) return gather_t<32>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, st, tm);
+  if (cpr >= 16) return gather_t<16>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, st, tm);
+  if (cpr >= 8) return gather_t<8>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, st, tm);
+  return gather_t<4>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, st, tm);
 }
 
 }  // namespace casgd

@@ -22,16 +22,19 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kTile = 64;  // output tile edge; 4 waves of 32 x 32
 
 // One 64 x 64 output tile per workgroup of 256 lanes; blockIdx.x enumerates
-// (block (j,t), tile row, tile col).  Rows past the block edge (b not a
-// multiple of 64) load as zeros and are not stored.  K is walked in BK-wide
+// (block (j,t), tile row, tile col).  Output rows and columns past the block
+// edge (b not a multiple of 64) are not stored.  K is walked in BK-wide
 // stages: each stage's global loads are issued D stages before it is used
 // (a ring of D register sets per lane), then the stage is copied into one of
-// two LDS buffers and consumed by the MFMAs.  Keeping D stages in flight
-// hides the memory latency that a one-stage prefetch leaves exposed.
+// two LDS buffers and consumed by the MFMAs.  Loads carry no branches and
+// their data is not touched until the LDS copy, so the compiler waits for
+// exactly the stage it needs and D stages stay in flight.  The stage count
+// is padded to a multiple of D with zero stages.
 template <int BK, int D>
 __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restrict__ Y,
                                                         int64_t ld, int b, int tps,
-                                                        float* __restrict__ G) {
+                                                        float* __restrict__ G,
+                                                        const int* __restrict__ order) {
   constexpr int CPR = BK / 8;          // 16-byte chunks per tile row per stage
   constexpr int RPP = 256 / CPR;       // tile rows loaded per pass
   constexpr int PASSES = kTile / RPP;  // passes per operand per stage
@@ -41,7 +44,8 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restri
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * LW];
 
   const int nt2 = tps * tps;
-  const int tile = blockIdx.x;
+  const int tile = order[blockIdx.x];  // XCD-grouped tile order; -1 pads the grid
+  if (tile < 0) return;
   const int p = tile / nt2;
   const int rem = tile - p * nt2;
   const int ti = rem / tps;
@@ -54,29 +58,37 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restri
   const int a0 = ti * kTile;  // first row of the A tile inside block-row j
   const int b0 = tj * kTile;  // first row of the B tile inside block-row t
 
+  // Rows past the block edge read rows of the same block instead; they only
+  // feed output rows / columns that are never stored.
   const int lrow = threadIdx.x / CPR;
   const int lchunk = threadIdx.x - lrow * CPR;
   const uint16_t* aptr[PASSES];
   const uint16_t* bptr[PASSES];
-  bool aok[PASSES], bok[PASSES];
 #pragma unroll
   for (int q = 0; q < PASSES; ++q) {
     const int r = lrow + q * RPP;
-    aok[q] = a0 + r < b;
-    bok[q] = b0 + r < b;
-    aptr[q] = Y + (static_cast<int64_t>(j) * b + a0 + (aok[q] ? r : 0)) * ld + lchunk * 8;
-    bptr[q] = Y + (static_cast<int64_t>(t) * b + b0 + (bok[q] ? r : 0)) * ld + lchunk * 8;
+    const int ar = a0 + r < b ? r : 0;
+    const int br = b0 + r < b ? r : 0;
+    aptr[q] = Y + (static_cast<int64_t>(j) * b + a0 + ar) * ld + lchunk * 8;
+    bptr[q] = Y + (static_cast<int64_t>(t) * b + b0 + br) * ld + lchunk * 8;
   }
 
+  // Chunks past the end of the row (a half-width last stage, or the zero
+  // stages that pad the count to a multiple of D) read column 0 and are
+  // zeroed when copied to LDS, D stages later, so no load waits early.
   u32x4 ra[D][PASSES], rb[D][PASSES];
+  bool kin[D];
   const int64_t nstage = (ld + BK - 1) / BK;
+  const int64_t nst_pad = (nstage + D - 1) / D * D;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
   auto load_stage = [&](int slot, int64_t st) {
     const int64_t k0 = st * BK;
-    const bool kin = k0 + lchunk * 8 < ld;  // last stage may be half-width
+    kin[slot] = k0 + lchunk * 8 < ld;
+    const int64_t off = kin[slot] ? k0 : 0;
 #pragma unroll
     for (int q = 0; q < PASSES; ++q) {
-      ra[slot][q] = (aok[q] && kin) ? *reinterpret_cast<const u32x4*>(aptr[q] + k0) : u32x4{0u, 0u, 0u, 0u};
-      rb[slot][q] = (bok[q] && kin) ? *reinterpret_cast<const u32x4*>(bptr[q] + k0) : u32x4{0u, 0u, 0u, 0u};
+      ra[slot][q] = *reinterpret_cast<const u32x4*>(aptr[q] + off);
+      rb[slot][q] = *reinterpret_cast<const u32x4*>(bptr[q] + off);
     }
   };
 
@@ -87,36 +99,42 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restri
   const int brow = wn * 32 + (lane & 31);
   const int kofs = (lane >> 5) * 8;
 
-  f32x16_t acc;
+  // one accumulator per 16-wide K slice of a stage: the MFMAs of a stage are
+  // independent and issue back to back instead of waiting on each other
+  constexpr int NACC = BK / 16;
+  f32x16_t acc[NACC];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int kk = 0; kk < NACC; ++kk)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[kk][e] = 0.f;
 
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < nstage) load_stage(d, d);
+  for (int d = 0; d < D; ++d) load_stage(d, d);
 
-  for (int64_t st0 = 0; st0 < nstage; st0 += D) {
+  for (int64_t st0 = 0; st0 < nst_pad; st0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int64_t cur = st0 + d;
-      if (cur >= nstage) break;
-      const int buf = static_cast<int>(cur & 1);
+      const int buf = static_cast<int>((st0 + d) & 1);
 #pragma unroll
       for (int q = 0; q < PASSES; ++q) {
         const int r = lrow + q * RPP;
-        *reinterpret_cast<u32x4*>(&As[buf][r * LW + lchunk * 8]) = ra[d][q];
-        *reinterpret_cast<u32x4*>(&Bs[buf][r * LW + lchunk * 8]) = rb[d][q];
+        *reinterpret_cast<u32x4*>(&As[buf][r * LW + lchunk * 8]) = kin[d] ? ra[d][q] : zero;
+        *reinterpret_cast<u32x4*>(&Bs[buf][r * LW + lchunk * 8]) = kin[d] ? rb[d][q] : zero;
       }
       __syncthreads();
-      if (cur + D < nstage) load_stage(d, cur + D);
+      load_stage(d, st0 + d + D);
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
+      for (int kk = 0; kk < NACC; ++kk) {
         const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&As[buf][arow * LW + kk * 16 + kofs]);
         const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][brow * LW + kk * 16 + kofs]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+        acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[kk], 0, 0, 0);
       }
     }
   }
+#pragma unroll
+  for (int kk = 1; kk < NACC; ++kk)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[0][e] += acc[kk][e];
 
   // Accumulator element e of lane l holds row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32 of the wave's 32 x 32 sub-tile.
@@ -126,7 +144,7 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restri
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int row = a0 + wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (row < b) gcol[row * ldg] = acc[e];
+      if (row < b) gcol[row * ldg] = acc[0][e];
     }
   }
 }
@@ -134,13 +152,16 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restri
 // float32 storage: the same tiles on the vector ALUs (each lane a 4 x 4
 // register block), used when the data are kept in float32.
 __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__ Y, int64_t ld,
-                                                       int b, int tps, float* __restrict__ G) {
+                                                       int b, int tps, float* __restrict__ G,
+                                                       const int* __restrict__ order) {
   constexpr int BK = 16;
   __shared__ float As[BK][kTile + 4];
   __shared__ float Bs[BK][kTile + 4];
   const int nt2 = tps * tps;
-  const int p = blockIdx.x / nt2;
-  const int rem = blockIdx.x - p * nt2;
+  const int tile = order[blockIdx.x];
+  if (tile < 0) return;
+  const int p = tile / nt2;
+  const int rem = tile - p * nt2;
   const int ti = rem / tps;
   const int tj = rem - ti * tps;
   int j, t;
@@ -205,23 +226,53 @@ GramPlan gram_plan(int storage, int s, int b, int64_t ld) {
   GramPlan p;
   const int tps = (b + kTile - 1) / kTile;
   p.tiles = s * (s - 1) / 2 * tps * tps;
+  p.slots = (p.tiles + kXcds - 1) / kXcds * kXcds;
   return p;
 }
 
+// Workgroups are dealt to the XCDs round-robin (workgroup w runs on XCD w mod
+// 8, each XCD with its own L2).  Tiles are listed in super-blocks of S x S
+// blocks (S chosen so a super-block holds about one XCD's share), the list is
+// cut into 8 consecutive runs, and run x is placed on the workgroups of XCD x:
+// the tiles that share rows of Y then share an L2.
+std::vector<int> gram_order(int s, int b) {
+  const int tps = (b + kTile - 1) / kTile;
+  const int tiles = s * (s - 1) / 2 * tps * tps;
+  const int per = (tiles + kXcds - 1) / kXcds;
+  int S = 1;
+  while (S < s && (S + 1) * (S + 1) * tps * tps <= per) ++S;
+  std::vector<int> list;
+  list.reserve(tiles);
+  for (int J = 0; J * S < s; ++J)
+    for (int T = 0; T <= J; ++T)
+      for (int j = J * S; j < (J + 1) * S && j < s; ++j)
+        for (int t = T * S; t < (T + 1) * S && t < j; ++t)
+          for (int q = 0; q < tps * tps; ++q) list.push_back((j * (j - 1) / 2 + t) * tps * tps + q);
+  std::vector<int> order(static_cast<size_t>(per) * kXcds, -1);
+  for (int x = 0; x < kXcds; ++x)
+    for (int k = 0; k < per; ++k) {
+      const int idx = x * per + k;
+      if (idx < tiles) order[static_cast<size_t>(k) * kXcds + x] = list[idx];
+    }
+  return order;
+}
+
 hipError_t launch_gram(int storage, const void* Y, int64_t ld, int s, int b, float* G,
-                       const GramPlan& plan, hipStream_t st) {
+                       const GramPlan& plan, const int* order, hipStream_t st, const LaunchTimer& tm) {
   (void)s;
   if (plan.tiles == 0) return hipSuccess;
   const int tps = (b + kTile - 1) / kTile;
+  const dim3 grid(static_cast<unsigned>(plan.slots));
   if (storage == kStoreBF16) {
-    if (ld > 32)
-      gram_bf16_kernel<64, 8><<<plan.tiles, 256, 0, st>>>(static_cast<const uint16_t*>(Y), ld, b, tps, G);
-    else
-      gram_bf16_kernel<32, 1><<<plan.tiles, 256, 0, st>>>(static_cast<const uint16_t*>(Y), ld, b, tps, G);
-  } else {
-    gram_f32_kernel<<<plan.tiles, 256, 0, st>>>(static_cast<const float*>(Y), ld, b, tps, G);
+    const uint16_t* Yb = static_cast<const uint16_t*>(Y);
+    if (ld <= 32) return launch_kernel(gram_bf16_kernel<32, 1>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
+    const int64_t nstage = (ld + 63) / 64;
+    if (nstage >= 8) return launch_kernel(gram_bf16_kernel<64, 8>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
+    if (nstage >= 4) return launch_kernel(gram_bf16_kernel<64, 4>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
+    return launch_kernel(gram_bf16_kernel<64, 2>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
   }
-  return hipGetLastError();
+  return launch_kernel(gram_f32_kernel, grid, dim3(256), 0, st, tm, static_cast<const float*>(Y), ld, b,
+                       tps, G, order);
 }
 
 }  // namespace casgd

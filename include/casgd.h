@@ -163,7 +163,8 @@ int64_t casgd_ld(casgd_handle h);
  */
 int64_t casgd_gram_bytes(int s, int b, int packed);
 
-/* Time every kernel launch with HIP events on the handle's stream (on != 0). */
+/* Time every hot-path kernel launch (on != 0) with HIP events that the
+ * kernel's own dispatch stamps at its start and end. */
 int casgd_set_timing(casgd_handle h, int on);
 
 /* Total milliseconds and launch count of one kernel (enum casgd_kernel_id)
