@@ -45,6 +45,32 @@ def algorithmic(wl):
     }
 
 
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gram_bf16_kernel-epsilon-pmc.md")
+GRAM_SOURCE = os.path.join(ROOT, "communication_avoiding_mixed_amd", "csrc", "k_gram.hip")
+
+
+def gram_traffic(workload: str):
+    """Scaled HBM bytes per Gram launch from the committed rocprofv3 --pmc
+    summary, or None if there is none for this workload or the kernel source
+    has changed since it was taken."""
+    import hashlib
+    if workload != "epsilon" or not os.path.exists(PMC_SUMMARY):
+        return None
+    vals = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip().strip("-* `")] = v.strip().strip("`")
+    sha = hashlib.sha256(open(GRAM_SOURCE, "rb").read()).hexdigest()
+    try:
+        if vals["kernel_source_sha256"] != sha:
+            return None
+        return (float(vals["fetch_kib_per_dispatch"]) * 1024 * float(vals["fetch_scale"])
+                + float(vals["write_kib_per_dispatch"]) * 1024 * float(vals["write_scale"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(X, y, wl, budget_s: float):
     """The oracle's outer step, as it stands, on the host: inner steps/s."""
     import numpy as np
@@ -173,6 +199,7 @@ def main():
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "traffic": None}
     roof["kernel"] = "gram_bf16_kernel"
+    roof["traffic"] = gram_traffic(wl.name)
 
     out = {
         "metric": METRIC,
