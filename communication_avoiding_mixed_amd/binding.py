@@ -21,6 +21,8 @@ BF16, FP32 = 0, 1
 OK, EINVAL, ENOMEM, EHIP = 0, -1, -2, -3
 EXPORT_IDX, EXPORT_Y, EXPORT_YB, EXPORT_G, EXPORT_V, EXPORT_Z, EXPORT_R = range(7)
 K_GATHER, K_GRAM, K_CHAIN = range(3)
+OPT_RECURRENCE = 0
+RECURRENCE_AUTO, RECURRENCE_ALL_TO_ALL, RECURRENCE_LOOKAHEAD = 0, 1, 2
 KERNEL_NAMES = {K_GATHER: "gather", K_GRAM: "gram", K_CHAIN: "chain"}
 
 LOSS_IDS = {"logistic": LOGISTIC, "squared": SQUARED, "poisson": POISSON}
@@ -45,6 +47,7 @@ SIGNATURES = {
     "casgd_get_timing": (_I, [_VP, _I, ctypes.POINTER(ctypes.c_double),
                               ctypes.POINTER(ctypes.c_int64), _I]),
     "casgd_last_error": (ctypes.c_char_p, []),
+    "casgd_set_option": (_I, [_VP, _I, _I]),
 }
 
 _lib = None
@@ -199,6 +202,9 @@ class CASGD:
                                         arr.ctypes.data_as(ctypes.c_void_p), arr.nbytes),
                "casgd_export_rows")
         return arr
+
+    def set_option(self, option: int, value: int):
+        _check(load().casgd_set_option(self._handle(), option, value), "casgd_set_option")
 
     def set_timing(self, on: bool):
         _check(load().casgd_set_timing(self._handle(), 1 if on else 0), "casgd_set_timing")

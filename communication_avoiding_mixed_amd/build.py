@@ -21,8 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcasgd.so")
 
-SOURCES = ["casgd_api.hip", "k_gather.hip", "k_gram.hip", "k_chain.hip", "k_loss.hip"]
-HEADERS = ["casgd_device.h", "casgd_internal.h"]
+SOURCES = ["casgd_api.hip", "k_gather.hip", "k_gram.hip", "k_chain.hip", "k_chain_la.hip", "k_loss.hip"]
+HEADERS = ["casgd_device.h", "casgd_internal.h", "casgd_chain.h"]
 
 ARCH = "gfx950"
 FLAGS = [

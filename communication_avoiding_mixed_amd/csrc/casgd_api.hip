@@ -76,6 +76,7 @@ struct casgd_ctx {
   double* loss_partial = nullptr;
   double* loss_out = nullptr;
   uint32_t epoch = 0;
+  int recurrence = 0;  // CASGD_OPT_RECURRENCE
 
   int next_buf = 0;
   int last_buf = 0;
@@ -274,8 +275,13 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   a.xbuf = h->xbuf;
   a.epoch = ++h->epoch == 0 ? ++h->epoch : h->epoch;
   a.status = h->status;
+  // The all-to-all kernel is the faster one on every measured shape, so it is
+  // the default; the lookahead form runs only when asked for.
+  const casgd::LaPlan la = h->recurrence == 2 ? casgd::la_plan(s, b) : casgd::LaPlan{};
+  if (la.ok) a.Q = casgd::kChainMaxWorkgroups;
   e = timed(h, CASGD_K_CHAIN, [&](const casgd::LaunchTimer& tm) {
-    return casgd::launch_chain(h->storage, h->loss, a, h->stream, tm);
+    return la.ok ? casgd::launch_chain_la(h->storage, h->loss, a, la, h->stream, tm)
+                 : casgd::launch_chain(h->storage, h->loss, a, h->stream, tm);
   });
   if (e != hipSuccess) return hip_fail(e, "recurrence launch");
   e = hipEventRecord(h->ev_chain[k], h->stream);
@@ -390,6 +396,15 @@ int casgd_set_stream(casgd_handle h, void* stream) {
 }
 
 int64_t casgd_ld(casgd_handle h) { return h ? h->ld : -1; }
+
+int casgd_set_option(casgd_handle h, int option, int value) {
+  if (!h) return fail(CASGD_EINVAL, "NULL handle");
+  if (option == CASGD_OPT_RECURRENCE && value >= 0 && value <= 2) {
+    h->recurrence = value;
+    return CASGD_OK;
+  }
+  return fail(CASGD_EINVAL, "unknown option or value");
+}
 
 int casgd_outer_step(casgd_handle h, int s, int b, float eta, uint64_t seed, float* w) {
   int rc = check_step_args(h, s, b, w);

@@ -1,0 +1,195 @@
+// Device building blocks shared by the two weight-dependent kernels (the
+// all-to-all recurrence in k_chain.hip and the lookahead recurrence in
+// k_chain_la.hip): widening of 16-byte chunks, tagged exchange words,
+// batched margins of a set of rows, and the column-sliced weight update.
+#pragma once
+
+#include "casgd_device.h"
+#include "casgd_internal.h"
+
+namespace casgd {
+namespace chain {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr long kSpinLimit = 1L << 22;  // polls: seconds, far above any real wait
+
+template <typename T>
+struct Elems;
+template <>
+struct Elems<uint16_t> {
+  static constexpr int E = 8;
+  __device__ static void widen(const u32x4& q, float (&f)[8]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
+      f[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+    }
+  }
+};
+template <>
+struct Elems<float> {
+  static constexpr int E = 4;
+  __device__ static void widen(const u32x4& q, float (&f)[4]) {
+    f[0] = __uint_as_float(q.x);
+    f[1] = __uint_as_float(q.y);
+    f[2] = __uint_as_float(q.z);
+    f[3] = __uint_as_float(q.w);
+  }
+};
+
+// A float r value travels with the launch's epoch in the upper half of a
+// 64-bit word, so a reader spins on the data itself.
+__device__ __forceinline__ uint64_t tagged(uint32_t epoch, float x) {
+  return (static_cast<uint64_t>(epoch) << 32) | __float_as_uint(x);
+}
+
+__device__ __forceinline__ void put(unsigned long long* p, uint64_t word) {
+  __hip_atomic_store(p, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin until *p carries `epoch`; returns its float.  Bounded: on expiry sets
+// *abort (LDS) and bit 0 of *status and returns 0.
+__device__ __forceinline__ float take(const unsigned long long* p, uint32_t epoch, int* status,
+                                      int* abort_flag, int sleep) {
+  long it = 0;
+  while (true) {
+    const uint64_t x = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (static_cast<uint32_t>(x >> 32) == epoch) return __uint_as_float(static_cast<uint32_t>(x));
+    if (++it > kSpinLimit) {
+      *abort_flag = 1;
+      atomicOr(status, 1);
+      return 0.f;
+    }
+    if (sleep) __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Margins x . w of `nrows` rows of Y, row number row_of(p) for p < nrows.
+// Each wave takes kRB rows at a time so their loads are in flight together.
+// lane 0 of the wave calls out(p, row, value).
+template <typename T, typename RowOf, typename Out>
+__device__ void margins(const T* Y, int64_t ld, int64_t n, const float* w, int nrows, RowOf row_of,
+                        Out out, int wave, int lane) {
+  constexpr int E = Elems<T>::E;
+  constexpr int kRB = 4;
+  const int64_t cpr = ld / E;
+  const bool w_vec = (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+  for (int p0 = wave * kRB; p0 < nrows; p0 += kWaves * kRB) {
+    float acc[kRB];
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) acc[r] = 0.f;
+    for (int64_t c0 = lane; c0 < cpr; c0 += 64 * 4) {
+      u32x4 qv[kRB][4];
+#pragma unroll
+      for (int r = 0; r < kRB; ++r) {
+        const int p = p0 + r;
+        const u32x4* yr = reinterpret_cast<const u32x4*>(Y + row_of(p < nrows ? p : p0) * ld);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t c = c0 + 64 * u;
+          qv[r][u] = (p < nrows && c < cpr) ? yr[c] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = c0 + 64 * u;
+        if (c >= cpr) break;
+        const int64_t col0 = c * E;
+        float wv[E];
+        if (w_vec && col0 + E <= n) {
+          const f32x4* w4 = reinterpret_cast<const f32x4*>(w + col0);
+#pragma unroll
+          for (int h = 0; h < E / 4; ++h) {
+            const f32x4 ww = w4[h];
+            wv[4 * h + 0] = ww.x;
+            wv[4 * h + 1] = ww.y;
+            wv[4 * h + 2] = ww.z;
+            wv[4 * h + 3] = ww.w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) wv[e] = col0 + e < n ? w[col0 + e] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < kRB; ++r) {
+          float f[E];
+          Elems<T>::widen(qv[r][u], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[r] = fmaf(f[e], wv[e], acc[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) {
+      const float tot = group_sum<64>(acc[r]);
+      const int p = p0 + r;
+      if (lane == 0 && p < nrows) out(p, row_of(p), tot);
+    }
+  }
+}
+
+// w[col] -= c * sum_rows Y[row][col] r[row] for the 16-byte column chunks
+// [q*per, (q+1)*per) of this workgroup (per = ceil(chunks / Q)).  Rows are
+// summed per thread in a fixed order, then across threads in a fixed order
+// through `red` (kThreads * E floats of LDS).  Must be called by the whole
+// workgroup; rs holds r for all sb rows.
+template <typename T>
+__device__ void update_columns(const T* Y, int64_t ld, int64_t n, int sb, const float* rs, float c,
+                               float* w, int q, int Q, float* red) {
+  constexpr int E = Elems<T>::E;
+  const int64_t cpr = ld / E;
+  const int64_t per = (cpr + Q - 1) / Q;
+  const int64_t ch0 = static_cast<int64_t>(q) * per;
+  const int64_t ch1 = ch0 + per < cpr ? ch0 + per : cpr;
+  int cw = 1;
+  while (cw < per && cw < 64) cw <<= 1;
+  const int rgn = kThreads / cw;
+  const int cl = threadIdx.x % cw;
+  const int rg = threadIdx.x / cw;
+  const u32x4* Y4 = reinterpret_cast<const u32x4*>(Y);
+  for (int64_t cb = ch0; cb < ch1; cb += cw) {
+    const int64_t ch = cb + cl;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    if (ch < ch1) {
+      int row = rg;
+      for (; row + 15 * rgn < sb; row += 16 * rgn) {
+        u32x4 qv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) qv[u] = Y4[static_cast<int64_t>(row + u * rgn) * cpr + ch];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          float f[E];
+          Elems<T>::widen(qv[u], f);
+          const float rr = rs[row + u * rgn];
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] = fmaf(f[e], rr, acc[e]);
+        }
+      }
+      for (; row < sb; row += rgn) {
+        float f[E];
+        Elems<T>::widen(Y4[static_cast<int64_t>(row) * cpr + ch], f);
+        const float rr = rs[row];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(f[e], rr, acc[e]);
+      }
+    }
+    __syncthreads();  // red is reused across column blocks
+#pragma unroll
+    for (int e = 0; e < E; ++e) red[rg * (cw * E) + cl * E + e] = acc[e];
+    __syncthreads();
+    for (int o = threadIdx.x; o < cw * E; o += kThreads) {
+      float sum = 0.f;
+      for (int g = 0; g < rgn; ++g) sum += red[g * (cw * E) + o];
+      const int64_t chunk = cb + o / E;
+      const int64_t col = chunk * E + o % E;
+      if (chunk < ch1 && col < n) w[col] = w[col] - c * sum;
+    }
+  }
+}
+
+}  // namespace chain
+}  // namespace casgd

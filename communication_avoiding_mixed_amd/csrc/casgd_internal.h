@@ -81,6 +81,19 @@ constexpr int kChainMaxWorkgroups = 64;
 hipError_t launch_chain(int storage, int loss, const ChainArgs& a, hipStream_t stream,
                         const LaunchTimer& tm = {});
 
+// Lookahead form of the same kernel (one critical workgroup for the d latest
+// blocks of every step, M helpers for the rest, receivers for the update);
+// ok is false for shapes it does not take (then launch_chain is used).
+struct LaPlan {
+  bool ok = false;
+  int d = 0;       // near blocks per step
+  int M = 0;       // helper workgroups (b / M rows each)
+  size_t lds = 0;  // dynamic LDS bytes per workgroup
+};
+LaPlan la_plan(int s, int b);
+hipError_t launch_chain_la(int storage, int loss, const ChainArgs& a, const LaPlan& plan,
+                           hipStream_t stream, const LaunchTimer& tm = {});
+
 // Mean loss over all m stored rows into out_dev (one double); partial must
 // hold kLossBlocks doubles.
 constexpr int kLossBlocks = 2048;

@@ -19,44 +19,16 @@
 // bounded: on expiry the kernel flags an error in `status` and returns.
 // After the last inner step every workgroup holds all of r and updates its
 // own slice of columns of w in a fixed summation order (no float atomics).
-#include "casgd_device.h"
-#include "casgd_internal.h"
+#include "casgd_chain.h"
 
 namespace casgd {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr long kSpinLimit = 1L << 25;
-
-template <typename T>
-struct Elems;
-template <>
-struct Elems<uint16_t> {
-  static constexpr int E = 8;
-  __device__ static void widen(const u32x4& q, float (&f)[8]) {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
-      f[2 * e + 1] = bf16_to_f32(w[e] >> 16);
-    }
-  }
-};
-template <>
-struct Elems<float> {
-  static constexpr int E = 4;
-  __device__ static void widen(const u32x4& q, float (&f)[4]) {
-    f[0] = __uint_as_float(q.x);
-    f[1] = __uint_as_float(q.y);
-    f[2] = __uint_as_float(q.z);
-    f[3] = __uint_as_float(q.w);
-  }
-};
-
-__device__ __forceinline__ uint64_t tagged(uint32_t epoch, float x) {
-  return (static_cast<uint64_t>(epoch) << 32) | __float_as_uint(x);
-}
+using chain::Elems;
+using chain::kSpinLimit;
+using chain::kThreads;
+using chain::kWaves;
+using chain::tagged;
 
 // LDS layout (floats): rs[sb] | vown[s * nown_max] | yown[s * nown_max] |
 // region, where region
@@ -83,7 +55,6 @@ __host__ __device__ inline ChainLayout chain_layout(int s, int b, int Q, bool pr
 template <typename T, int LOSS>
 __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
-  constexpr int E = Elems<T>::E;
   const int s = a.s, b = a.b, Q = a.Q;
   const int sb = s * b;
   const int q = blockIdx.x;
@@ -99,8 +70,6 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   if (threadIdx.x == 0) abort_flag = 0;
 
   const T* Y = static_cast<const T*>(a.Y);
-  const int64_t cpr = a.ld / E;  // 16-byte chunks per row
-  const bool w_vec = (reinterpret_cast<uintptr_t>(a.w) & 15) == 0;
   const int64_t P = static_cast<int64_t>(b) * (static_cast<int64_t>(s) * (s - 1) / 2);
 
   // ---- this workgroup's rows of every block-row of G into LDS, 16 loads in
@@ -138,72 +107,19 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     }
   }
 
-  // ---- margins of the own rows: each wave takes kRB rows at a time so that
-  // all of their loads are in flight together
-  constexpr int kRB = 4;
-  const int nrows_own = s * nown;
-  for (int p0 = wave * kRB; p0 < nrows_own; p0 += kWaves * kRB) {
-    float acc[kRB];
-#pragma unroll
-    for (int r = 0; r < kRB; ++r) acc[r] = 0.f;
-    for (int64_t c0 = lane; c0 < cpr; c0 += 64 * 4) {
-      u32x4 qv[kRB][4];
-#pragma unroll
-      for (int r = 0; r < kRB; ++r) {
-        const int p = p0 + r;
+  // ---- margins of the own rows (row p = (j, t) is minibatch j's row q + Q t)
+  chain::margins<T>(
+      Y, a.ld, a.n, a.w, s * nown,
+      [&](int p) {
         const int j = p / nown;
-        const int t = p - j * nown;
-        const u32x4* yr = reinterpret_cast<const u32x4*>(
-            Y + (static_cast<int64_t>(j) * b + q + static_cast<int64_t>(Q) * t) * a.ld);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t c = c0 + 64 * u;
-          qv[r][u] = (p < nrows_own && c < cpr) ? yr[c] : u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t c = c0 + 64 * u;
-        if (c >= cpr) break;
-        const int64_t col0 = c * E;
-        float wv[E];
-        if (w_vec && col0 + E <= a.n) {
-          const f32x4* w4 = reinterpret_cast<const f32x4*>(a.w + col0);
-#pragma unroll
-          for (int h = 0; h < E / 4; ++h) {
-            const f32x4 ww = w4[h];
-            wv[4 * h + 0] = ww.x;
-            wv[4 * h + 1] = ww.y;
-            wv[4 * h + 2] = ww.z;
-            wv[4 * h + 3] = ww.w;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < E; ++e) wv[e] = col0 + e < a.n ? a.w[col0 + e] : 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < kRB; ++r) {
-          float f[E];
-          Elems<T>::widen(qv[r][u], f);
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[r] = fmaf(f[e], wv[e], acc[r]);
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kRB; ++r) {
-      const float tot = group_sum<64>(acc[r]);
-      const int p = p0 + r;
-      if (lane == 0 && p < nrows_own) {
-        const int j = p / nown;
-        const int t = p - j * nown;
-        const int64_t row = static_cast<int64_t>(j) * b + q + static_cast<int64_t>(Q) * t;
-        vown[p] = tot;
+        return static_cast<int64_t>(j) * b + q + static_cast<int64_t>(Q) * (p - j * nown);
+      },
+      [&](int p, int64_t row, float v) {
+        vown[p] = v;
         yown[p] = a.yB[row];
-        a.v[row] = tot;
-      }
-    }
-  }
+        a.v[row] = v;
+      },
+      wave, lane);
   __syncthreads();  // vown and the G rows ready
 
   // ---- inner recurrence.  Waves 1..3 compute and publish the own rows;
@@ -292,57 +208,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     if (abort_flag) return;
   }
 
-  // ---- update: w[col] -= c * sum_rows Y[row][col] r[row] on this workgroup's columns
-  float* red = gl;  // the G rows are no longer needed
-  const int64_t per = (cpr + Q - 1) / Q;
-  const int64_t ch0 = static_cast<int64_t>(q) * per;
-  const int64_t ch1 = ch0 + per < cpr ? ch0 + per : cpr;
-  int cw = 1;
-  while (cw < per && cw < 64) cw <<= 1;
-  const int rgn = kThreads / cw;
-  const int cl = threadIdx.x % cw;
-  const int rg = threadIdx.x / cw;
-  const u32x4* Y4 = reinterpret_cast<const u32x4*>(Y);
-  for (int64_t cb = ch0; cb < ch1; cb += cw) {
-    const int64_t ch = cb + cl;
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    if (ch < ch1) {
-      int row = rg;
-      for (; row + 15 * rgn < sb; row += 16 * rgn) {
-        u32x4 qv[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) qv[u] = Y4[static_cast<int64_t>(row + u * rgn) * cpr + ch];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          float f[E];
-          Elems<T>::widen(qv[u], f);
-          const float rr = rs[row + u * rgn];
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[e] = fmaf(f[e], rr, acc[e]);
-        }
-      }
-      for (; row < sb; row += rgn) {
-        float f[E];
-        Elems<T>::widen(Y4[static_cast<int64_t>(row) * cpr + ch], f);
-        const float rr = rs[row];
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(f[e], rr, acc[e]);
-      }
-    }
-    __syncthreads();  // red is reused across column blocks
-#pragma unroll
-    for (int e = 0; e < E; ++e) red[rg * (cw * E) + cl * E + e] = acc[e];
-    __syncthreads();
-    for (int o = threadIdx.x; o < cw * E; o += kThreads) {
-      float sum = 0.f;
-      for (int g = 0; g < rgn; ++g) sum += red[g * (cw * E) + o];
-      const int64_t chunk = cb + o / E;
-      const int64_t col = chunk * E + o % E;
-      if (chunk < ch1 && col < a.n) a.w[col] = a.w[col] - a.c * sum;
-    }
-  }
+  // ---- update of this workgroup's columns of w; the G rows are no longer needed
+  chain::update_columns<T>(Y, a.ld, a.n, sb, rs, a.c, a.w, q, Q, gl);
 }
 
 template <typename T, int LOSS>

@@ -163,6 +163,24 @@ int64_t casgd_ld(casgd_handle h);
  */
 int64_t casgd_gram_bytes(int s, int b, int packed);
 
+/* Options (casgd_set_option). */
+enum casgd_option {
+  /* How the inner recurrence is spread over workgroups:
+   *   0 (default) the fastest form for the shape, currently always 1;
+   *   1 every workgroup owns rows of every minibatch and all exchange r each
+   *     inner step;
+   *   2 lookahead: one workgroup computes every step from the latest blocks
+   *     of G while helper workgroups add the older blocks ahead of time
+   *     (taken for 16 <= b <= 64, b a multiple of 16, s >= 2; otherwise 1).
+   * All forms give bit-identical results for a given shape and form; the
+   * forms differ from each other only in float32 rounding order. */
+  CASGD_OPT_RECURRENCE = 0
+};
+
+/* Set an option of the handle; later outer steps use it.  EINVAL for an
+ * unknown option or value. */
+int casgd_set_option(casgd_handle h, int option, int value);
+
 /* Time every hot-path kernel launch (on != 0) with HIP events that the
  * kernel's own dispatch stamps at its start and end. */
 int casgd_set_timing(casgd_handle h, int on);

@@ -23,9 +23,11 @@ def _targets(loss, m, seed):
     return rng.poisson(1.0, m).astype(np.float32)
 
 
-def run_and_compare(X, y, loss, s, b, eta, w0, seed=123, storage="bf16", idx=None):
+def run_and_compare(X, y, loss, s, b, eta, w0, seed=123, storage="bf16", idx=None, rec=None):
     import torch
     h = B.CASGD(torch_dev(X), torch_dev(y), loss, storage)
+    if rec is not None:
+        h.set_option(B.OPT_RECURRENCE, rec)
     w = torch_dev(w0)
     if idx is None:
         h.outer_step(s, b, eta, seed, w)
@@ -63,6 +65,22 @@ def test_ragged_and_degenerate_shapes(loss, m, n, s, b):
     if s == 1:
         assert h.export(B.EXPORT_G).size == 0
         assert np.array_equal(h.export(B.EXPORT_Z), h.export(B.EXPORT_V))
+
+
+@pytest.mark.parametrize("rec", [B.RECURRENCE_ALL_TO_ALL, B.RECURRENCE_LOOKAHEAD])
+@pytest.mark.parametrize("loss", ["logistic", "squared", "poisson"])
+@pytest.mark.parametrize("m,n,s,b", [
+    (2000, 40, 2, 16),    # one near block per step
+    (3000, 100, 5, 32),   # three near blocks, ragged K
+    (5000, 64, 20, 64),   # helpers own 2 rows each (LDS), far sums over 16 steps
+    (4000, 72, 30, 48),   # helpers own 1 row each
+    (3000, 50, 9, 64),    # b at the lookahead limit, ld 64
+])
+def test_lookahead_and_all_to_all_recurrences(loss, m, n, s, b, rec):
+    X = synth.make_uniform((m, n), seed=m + s, lo=-0.4, hi=0.4)
+    y = _targets(loss, m, seed=b)
+    w0 = synth.make_uniform((n,), seed=3, lo=-0.3, hi=0.3)
+    run_and_compare(X, y, loss, s, b, 0.2 if loss != "poisson" else 0.05, w0, rec=rec)
 
 
 def test_fp32_storage_ragged():
@@ -165,6 +183,20 @@ def test_repeatable_and_resumable():
     for k in range(20):
         h.outer_step(wl.s, wl.b, wl.eta, O.step_seed(0, k), w5)
     assert torch.equal(w5, w1)
+
+
+def test_lookahead_repeatable_and_resumable():
+    import torch
+    name = "epsilon"
+    wl = synth.WORKLOADS[name]
+    X, y = synth.make_data(name, m=20_000)
+    h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss)
+    w1 = torch.zeros(wl.n, device="cuda")
+    h.train(wl.s, wl.b, wl.eta, 0, 0, 12, w1)
+    w2 = torch.zeros(wl.n, device="cuda")
+    h.train(wl.s, wl.b, wl.eta, 0, 0, 6, w2)
+    h.train(wl.s, wl.b, wl.eta, 0, 6, 6, w2)
+    assert torch.equal(w1, w2)
 
 
 def test_side_stream_and_timing():

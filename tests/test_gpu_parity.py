@@ -81,10 +81,19 @@ def test_sample_and_gather_bit_exact(name):
     assert np.array_equal(yB, y[ref_idx])
 
 
+RECURRENCES = {"auto": B.RECURRENCE_AUTO, "all-to-all": B.RECURRENCE_ALL_TO_ALL,
+               "lookahead": B.RECURRENCE_LOOKAHEAD}
+
+
 @pytest.mark.parametrize("w0kind", ["zero", "seeded"])
-@pytest.mark.parametrize("name,storage", [(n, None) for n in SMALL] + [("logistic-4096x64", "fp32")])
-def test_outer_step_parity(name, storage, w0kind):
+@pytest.mark.parametrize("name,storage,rec", [(n, None, "auto") for n in SMALL] +
+                         [("logistic-4096x64", "fp32", "auto"),
+                          ("logistic-4096x64", None, "all-to-all"),
+                          ("epsilon", None, "all-to-all"),
+                          ("epsilon", None, "lookahead")])
+def test_outer_step_parity(name, storage, rec, w0kind):
     h, X, y, wl = handle(name, storage)
+    h.set_option(B.OPT_RECURRENCE, RECURRENCES[rec])
     st = storage or wl.storage
     w0 = np.zeros(wl.n, np.float32) if w0kind == "zero" else synth.make_w0(name, 1)
     w = torch_dev(w0)
@@ -98,7 +107,8 @@ def test_outer_step_parity(name, storage, w0kind):
     errs["z"] = rel_l2(h.export(B.EXPORT_Z), ref["z"])
     errs["r"] = rel_l2(h.export(B.EXPORT_R), ref["r"])
     errs["w"] = rel_l2(w.cpu().numpy(), ref["w"])
-    print(name, st, w0kind, {k: f"{v:.2e}" for k, v in errs.items()})
+    h.set_option(B.OPT_RECURRENCE, B.RECURRENCE_AUTO)
+    print(name, st, rec, w0kind, {k: f"{v:.2e}" for k, v in errs.items()})
     for k, e in errs.items():
         assert e <= REL_TOL, (k, e)
 
