@@ -19,6 +19,7 @@
 
 #include "casgd.h"
 #include "casgd_device.h"
+#include "casgd_gather.h"
 #include "casgd_internal.h"
 
 namespace {
@@ -35,6 +36,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int kMaxSB = 16384;
+constexpr int kPipeGatherWgs = 64;  // gather workgroups of a pipelined step launch
 
 struct EventPair {
   hipEvent_t start = nullptr;
@@ -64,7 +66,7 @@ struct casgd_ctx {
   // workspace, sized for cap_sb rows and cap_g Gram elements
   int cap_sb = 0;
   int64_t cap_g = 0;
-  StepBuffers buf[2];
+  StepBuffers buf[3];  // outer steps use sets 0 and 1; casgd_train's pipeline all three
   float* v = nullptr;
   float* z = nullptr;
   float* r = nullptr;
@@ -294,6 +296,109 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   return CASGD_OK;
 }
 
+// casgd_train's pipelined loop (bf16 storage, all-to-all recurrence): step i
+// uses buffer set i mod 3.  Prologue: gather and Gram of step 0, gather of
+// step 1.  Launch i: chain of step i, Gram of step i+1, gather of step i+2.
+// The gather of step i+2 overwrites the set of step i-1, whose chain ended
+// with the previous launch; everything runs on the caller's stream.
+int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, uint64_t first,
+                   int n, float* w) {
+  int rc = ensure_workspace(h, s, b);
+  if (rc != CASGD_OK) return rc;
+  rc = ensure_order(h, s, b);
+  if (rc != CASGD_OK) return rc;
+  const int sb = s * b;
+  const float c = eta / static_cast<float>(b);
+  auto seed_of = [&](int i) { return casgd::splitmix64(base_seed, first + static_cast<uint64_t>(i)); };
+  hipError_t e;
+
+  // work queued earlier on the prep stream reads or writes sets 0 and 1
+  e = hipEventRecord(h->ev_prep[0], h->prep);
+  if (e == hipSuccess) e = hipStreamWaitEvent(h->stream, h->ev_prep[0], 0);
+  if (e != hipSuccess) return hip_fail(e, "ordering the prep stream before the pipeline");
+
+  auto gather = [&](int i) {
+    StepBuffers& A = h->buf[i % 3];
+    return timed(h, CASGD_K_GATHER, [&](const casgd::LaunchTimer& tm) {
+      return casgd::launch_gather(h->storage, h->Xs, h->y, h->m, h->ld, sb, seed_of(i), nullptr, A.idx,
+                                  A.Y, A.yB, h->stream, tm);
+    });
+  };
+  const casgd::GramPlan plan = casgd::gram_plan(h->storage, s, b, h->ld);
+  e = gather(0);
+  if (e == hipSuccess)
+    e = timed(h, CASGD_K_GRAM, [&](const casgd::LaunchTimer& tm) {
+      return casgd::launch_gram(h->storage, h->buf[0].Y, h->ld, s, b, h->buf[0].G, plan, h->order,
+                                h->stream, tm);
+    });
+  if (e == hipSuccess && n > 1) e = gather(1);
+  if (e != hipSuccess) return hip_fail(e, "pipeline prologue");
+
+  const int Q = casgd::chain_workgroups(s, b);
+  const int64_t cpr = h->ld / 8;
+  const int gs = casgd::gather::group_size(cpr);
+  const int rows_per_wg = 256 / gs;
+  const int gather_wgs_all = (sb + rows_per_wg - 1) / rows_per_wg;
+  for (int i = 0; i < n; ++i) {
+    StepBuffers& C = h->buf[i % 3];
+    casgd::PipeArgs p;
+    casgd::ChainArgs& a = p.a;
+    a.Y = C.Y;
+    a.ld = h->ld;
+    a.n = h->n;
+    a.s = s;
+    a.b = b;
+    a.Q = Q;
+    a.c = c;
+    a.G = C.G;
+    a.yB = C.yB;
+    a.v = h->v;
+    a.z = h->z;
+    a.r = h->r;
+    a.w = w;
+    a.xbuf = h->xbuf;
+    a.epoch = ++h->epoch == 0 ? ++h->epoch : h->epoch;
+    a.status = h->status;
+    a.preload = 0;
+    p.gram0 = (Q + casgd::kXcds - 1) / casgd::kXcds * casgd::kXcds;
+    if (i + 1 < n && plan.tiles > 0) {
+      const StepBuffers& N = h->buf[(i + 1) % 3];
+      p.gram_slots = plan.slots;
+      p.tps = (b + 63) / 64;
+      p.gY = static_cast<const uint16_t*>(N.Y);
+      p.gG = N.G;
+      p.order = h->order;
+    }
+    p.gath0 = p.gram0 + p.gram_slots;
+    if (i + 2 < n) {
+      StepBuffers& A = h->buf[(i + 2) % 3];
+      p.gath_wgs = gather_wgs_all < kPipeGatherWgs ? gather_wgs_all : kPipeGatherWgs;
+      p.gs = gs;
+      p.Xs = h->Xs;
+      p.y = h->y;
+      p.m = h->m;
+      p.cpr = cpr;
+      p.sb = sb;
+      p.seed = seed_of(i + 2);
+      p.idx_out = A.idx;
+      p.Yo = A.Y;
+      p.yBo = A.yB;
+    }
+    e = timed(h, CASGD_K_PIPE, [&](const casgd::LaunchTimer& tm) {
+      return casgd::launch_pipe(h->loss, p, h->stream, tm);
+    });
+    if (e != hipSuccess) return hip_fail(e, "pipelined step launch");
+  }
+  // later outer steps' prep work reuses sets 0 and 1 only after this loop
+  e = hipEventRecord(h->ev_chain[0], h->stream);
+  if (e == hipSuccess) e = hipEventRecord(h->ev_chain[1], h->stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  h->last_buf = (n - 1) % 3;
+  h->last_s = s;
+  h->last_b = b;
+  return CASGD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -440,6 +545,8 @@ int casgd_train(casgd_handle h, int s, int b, float eta, uint64_t base_seed, uin
   int rc = check_step_args(h, s, b, w);
   if (rc != CASGD_OK) return rc;
   if (n_outer < 0) return fail(CASGD_EINVAL, "n_outer must be >= 0");
+  if (n_outer > 0 && h->storage == CASGD_BF16 && h->recurrence != 2)
+    return run_train_pipe(h, s, b, eta, base_seed, first_step, n_outer, w);
   for (int k = 0; k < n_outer; ++k) {
     rc = run_outer(h, s, b, eta, casgd::splitmix64(base_seed, first_step + k), nullptr, w);
     if (rc != CASGD_OK) return rc;

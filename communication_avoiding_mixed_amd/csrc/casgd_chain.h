@@ -70,7 +70,7 @@ __device__ __forceinline__ float take(const unsigned long long* p, uint32_t epoc
 // Each wave takes kRB rows at a time so their loads are in flight together.
 // lane 0 of the wave calls out(p, row, value).
 template <typename T, typename RowOf, typename Out>
-__device__ void margins(const T* Y, int64_t ld, int64_t n, const float* w, int nrows, RowOf row_of,
+__device__ __forceinline__ void margins(const T* Y, int64_t ld, int64_t n, const float* w, int nrows, RowOf row_of,
                         Out out, int wave, int lane) {
   constexpr int E = Elems<T>::E;
   constexpr int kRB = 4;
@@ -131,13 +131,17 @@ __device__ void margins(const T* Y, int64_t ld, int64_t n, const float* w, int n
 }
 
 // w[col] -= c * sum_rows Y[row][col] r[row] for the 16-byte column chunks
-// [q*per, (q+1)*per) of this workgroup (per = ceil(chunks / Q)).  Rows are
-// summed per thread in a fixed order, then across threads in a fixed order
-// through `red` (kThreads * E floats of LDS).  Must be called by the whole
-// workgroup; rs holds r for all sb rows.
+// [q*per, (q+1)*per) of this workgroup (per = ceil(chunks / Q)).  Thread
+// (rg, cl) sums rows rg, rg + rgn, ... of chunk cl in a fixed order; the row
+// groups of a wave are then added by an xor butterfly (every lane ends with
+// the same, order-independent value: each level adds two equal-rank partial
+// sums, a commutative step), and the four wave sums through `red`
+// (kWaves * 64 * E floats of LDS) in a fixed order.  No float atomics: the
+// result is bit-reproducible.  Must be called by the whole workgroup; rs
+// holds r for all sb rows.
 template <typename T>
-__device__ void update_columns(const T* Y, int64_t ld, int64_t n, int sb, const float* rs, float c,
-                               float* w, int q, int Q, float* red) {
+__device__ __forceinline__ void update_columns(const T* Y, int64_t ld, int64_t n, int sb, const float* rs,
+                                               float c, float* w, int q, int Q, float* red) {
   constexpr int E = Elems<T>::E;
   const int64_t cpr = ld / E;
   const int64_t per = (cpr + Q - 1) / Q;
@@ -148,6 +152,8 @@ __device__ void update_columns(const T* Y, int64_t ld, int64_t n, int sb, const 
   const int rgn = kThreads / cw;
   const int cl = threadIdx.x % cw;
   const int rg = threadIdx.x / cw;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const u32x4* Y4 = reinterpret_cast<const u32x4*>(Y);
   for (int64_t cb = ch0; cb < ch1; cb += cw) {
     const int64_t ch = cb + cl;
@@ -177,13 +183,18 @@ __device__ void update_columns(const T* Y, int64_t ld, int64_t n, int sb, const 
         for (int e = 0; e < E; ++e) acc[e] = fmaf(f[e], rr, acc[e]);
       }
     }
-    __syncthreads();  // red is reused across column blocks
+    // row groups of this wave: lanes cl, cl + cw, ... hold the same chunk
+    for (int off = cw; off < 64; off <<= 1)
 #pragma unroll
-    for (int e = 0; e < E; ++e) red[rg * (cw * E) + cl * E + e] = acc[e];
+      for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+    __syncthreads();  // red is reused across column blocks
+    if (lane < cw)
+#pragma unroll
+      for (int e = 0; e < E; ++e) red[wave * (64 * E) + lane * E + e] = acc[e];
     __syncthreads();
     for (int o = threadIdx.x; o < cw * E; o += kThreads) {
-      float sum = 0.f;
-      for (int g = 0; g < rgn; ++g) sum += red[g * (cw * E) + o];
+      float sum = red[o];
+      for (int g = 1; g < kWaves; ++g) sum += red[g * (64 * E) + o];
       const int64_t chunk = cb + o / E;
       const int64_t col = chunk * E + o % E;
       if (chunk < ch1 && col < n) w[col] = w[col] - c * sum;

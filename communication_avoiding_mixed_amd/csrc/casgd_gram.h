@@ -1,0 +1,154 @@
+// One 64 x 64 output tile of the strictly-lower block triangle of G = Y Y^T
+// on bf16 MFMA (v_mfma_f32_32x32x16_bf16, float32 accumulators), as a device
+// function so both the stand-alone Gram kernel and the pipelined step kernel
+// run the same code.  The Abstract of "Mixed-Precision Communication-Avoiding
+// SGD for Generalized Linear Models on GPUs" forms the Gram from low-precision
+// inputs with high-precision accumulation on the matrix hardware.
+//
+// Output layout (block-row): block-row j (1 <= j < s) is the b x (j*b)
+// row-major matrix [G_{j,0} ... G_{j,j-1}] starting at element b*b*j(j-1)/2.
+#pragma once
+
+#include "casgd_device.h"
+
+namespace casgd {
+namespace gram {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kTile = 64;  // output tile edge; 4 waves of 32 x 32
+
+// LDS the tile function needs: two buffers of A and of B, kTile rows of
+// BK + 8 bf16 each (the pad breaks bank aliasing).
+template <int BK>
+constexpr int lds_elems() {
+  return 2 * 2 * kTile * (BK + 8);
+}
+
+// Tile `tile` enumerates (block (j,t), tile row, tile col); a workgroup of
+// 256 lanes computes it.  Output rows and columns past the block edge (b not
+// a multiple of 64) are not stored.  K is walked in BK-wide stages: each
+// stage's global loads are issued D stages before it is used (a ring of D
+// register sets per lane), then the stage is copied into one of two LDS
+// buffers and consumed by the MFMAs.  Loads carry no branches and their data
+// is not touched until the LDS copy, so the compiler waits for exactly the
+// stage it needs and D stages stay in flight.  The stage count is padded to a
+// multiple of D with zero stages.  `lds` holds lds_elems<BK>() elements.
+template <int BK, int D>
+__device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ Y, int64_t ld, int b, int tps,
+                                          float* __restrict__ G, int tile, uint16_t* lds) {
+  constexpr int CPR = BK / 8;          // 16-byte chunks per tile row per stage
+  constexpr int RPP = 256 / CPR;       // tile rows loaded per pass
+  constexpr int PASSES = kTile / RPP;  // passes per operand per stage
+  constexpr int LW = BK + 8;           // LDS row pitch (elements)
+  constexpr int BUF = kTile * LW;
+  uint16_t* As = lds;            // [2][BUF]
+  uint16_t* Bs = lds + 2 * BUF;  // [2][BUF]
+
+  const int nt2 = tps * tps;
+  const int p = tile / nt2;
+  const int rem = tile - p * nt2;
+  const int ti = rem / tps;
+  const int tj = rem - ti * tps;
+  int j, t;
+  block_of(p, j, t);
+
+  float* Gj = G + static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
+  const int64_t ldg = static_cast<int64_t>(j) * b;
+  const int a0 = ti * kTile;  // first row of the A tile inside block-row j
+  const int b0 = tj * kTile;  // first row of the B tile inside block-row t
+
+  // Rows past the block edge read rows of the same block instead; they only
+  // feed output rows / columns that are never stored.
+  const int lrow = threadIdx.x / CPR;
+  const int lchunk = threadIdx.x - lrow * CPR;
+  const uint16_t* aptr[PASSES];
+  const uint16_t* bptr[PASSES];
+#pragma unroll
+  for (int q = 0; q < PASSES; ++q) {
+    const int r = lrow + q * RPP;
+    const int ar = a0 + r < b ? r : 0;
+    const int br = b0 + r < b ? r : 0;
+    aptr[q] = Y + (static_cast<int64_t>(j) * b + a0 + ar) * ld + lchunk * 8;
+    bptr[q] = Y + (static_cast<int64_t>(t) * b + b0 + br) * ld + lchunk * 8;
+  }
+
+  // Chunks past the end of the row (a half-width last stage, or the zero
+  // stages that pad the count to a multiple of D) read column 0 and are
+  // zeroed when copied to LDS, D stages later, so no load waits early.
+  u32x4 ra[D][PASSES], rb[D][PASSES];
+  bool kin[D];
+  const int64_t nstage = (ld + BK - 1) / BK;
+  const int64_t nst_pad = (nstage + D - 1) / D * D;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto load_stage = [&](int slot, int64_t st) {
+    const int64_t k0 = st * BK;
+    kin[slot] = k0 + lchunk * 8 < ld;
+    const int64_t off = kin[slot] ? k0 : 0;
+#pragma unroll
+    for (int q = 0; q < PASSES; ++q) {
+      ra[slot][q] = *reinterpret_cast<const u32x4*>(aptr[q] + off);
+      rb[slot][q] = *reinterpret_cast<const u32x4*>(bptr[q] + off);
+    }
+  };
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int arow = wm * 32 + (lane & 31);
+  const int brow = wn * 32 + (lane & 31);
+  const int kofs = (lane >> 5) * 8;
+
+  // one accumulator per 16-wide K slice of a stage: the MFMAs of a stage are
+  // independent and issue back to back instead of waiting on each other
+  constexpr int NACC = BK / 16;
+  f32x16_t acc[NACC];
+#pragma unroll
+  for (int kk = 0; kk < NACC; ++kk)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[kk][e] = 0.f;
+
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_stage(d, d);
+
+  for (int64_t st0 = 0; st0 < nst_pad; st0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int buf = static_cast<int>((st0 + d) & 1);
+#pragma unroll
+      for (int q = 0; q < PASSES; ++q) {
+        const int r = lrow + q * RPP;
+        *reinterpret_cast<u32x4*>(&As[buf * BUF + r * LW + lchunk * 8]) = kin[d] ? ra[d][q] : zero;
+        *reinterpret_cast<u32x4*>(&Bs[buf * BUF + r * LW + lchunk * 8]) = kin[d] ? rb[d][q] : zero;
+      }
+      __syncthreads();
+      load_stage(d, st0 + d + D);
+#pragma unroll
+      for (int kk = 0; kk < NACC; ++kk) {
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&As[buf * BUF + arow * LW + kk * 16 + kofs]);
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&Bs[buf * BUF + brow * LW + kk * 16 + kofs]);
+        acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[kk], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int kk = 1; kk < NACC; ++kk)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[0][e] += acc[kk][e];
+
+  // Accumulator element e of lane l holds row 8*(e/4) + 4*(l/32) + e%4,
+  // column l%32 of the wave's 32 x 32 sub-tile.
+  const int col = b0 + wn * 32 + (lane & 31);
+  if (col < b) {
+    float* gcol = Gj + static_cast<int64_t>(t) * b + col;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = a0 + wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (row < b) gcol[row * ldg] = acc[0][e];
+    }
+  }
+}
+
+}  // namespace gram
+}  // namespace casgd

@@ -52,6 +52,13 @@ struct GramPlan {
   int slots = 0;  // workgroups launched: tiles rounded up to a multiple of kXcds
 };
 GramPlan gram_plan(int storage, int s, int b, int64_t ld);
+// bf16 tile variant for rows of ld elements: 0 -> 32-wide K stages, one in
+// flight (ld <= 32); 1, 2, 3 -> 64-wide stages, 8, 4 or 2 in flight.
+inline int gram_variant(int64_t ld) {
+  if (ld <= 32) return 0;
+  const int64_t nstage = (ld + 63) / 64;
+  return nstage >= 8 ? 1 : nstage >= 4 ? 2 : 3;
+}
 std::vector<int> gram_order(int s, int b);
 hipError_t launch_gram(int storage, const void* Y, int64_t ld, int s, int b, float* G,
                        const GramPlan& plan, const int* order, hipStream_t stream,
@@ -80,6 +87,30 @@ int chain_workgroups(int s, int b);
 constexpr int kChainMaxWorkgroups = 64;
 hipError_t launch_chain(int storage, int loss, const ChainArgs& a, hipStream_t stream,
                         const LaunchTimer& tm = {});
+
+// One launch of the pipelined training loop (bf16 storage): the chain of
+// outer step k on workgroups [0, a.Q), the Gram of step k+1 (gram_slots > 0)
+// on [gram0, gram0 + gram_slots) with gram0 a multiple of kXcds, and the
+// sample + gather of step k+2 (gath_wgs > 0) on [gath0, gath0 + gath_wgs).
+// The three roles use disjoint buffers; Y/G/yB of the chain, Y/G of the Gram
+// and idx/Y/yB of the gather belong to three different steps.
+struct PipeArgs {
+  ChainArgs a;
+  int gram0 = 0, gram_slots = 0, tps = 0;
+  const uint16_t* gY = nullptr;  // Y of step k+1
+  float* gG = nullptr;           // G of step k+1
+  const int* order = nullptr;
+  int gath0 = 0, gath_wgs = 0, gs = 0;  // gs: lanes per row (gather::group_size)
+  const void* Xs = nullptr;
+  const float* y = nullptr;
+  int64_t m = 0, cpr = 0;
+  int sb = 0;
+  uint64_t seed = 0;  // seed of step k+2
+  int32_t* idx_out = nullptr;
+  void* Yo = nullptr;
+  float* yBo = nullptr;
+};
+hipError_t launch_pipe(int loss, const PipeArgs& p, hipStream_t stream, const LaunchTimer& tm = {});
 
 // Lookahead form of the same kernel (one critical workgroup for the d latest
 // blocks of every step, M helpers for the rest, receivers for the update);

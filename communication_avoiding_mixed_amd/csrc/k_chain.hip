@@ -20,6 +20,8 @@
 // After the last inner step every workgroup holds all of r and updates its
 // own slice of columns of w in a fixed summation order (no float atomics).
 #include "casgd_chain.h"
+#include "casgd_gather.h"
+#include "casgd_gram.h"
 
 namespace casgd {
 namespace {
@@ -31,185 +33,499 @@ using chain::kWaves;
 using chain::tagged;
 
 // LDS layout (floats): rs[sb] | vown[s * nown_max] | yown[s * nown_max] |
-// region, where region
-// holds this workgroup's rows of G (when a.preload) during the recurrence and
-// the update's reduction scratch afterwards.
+// acc[s * nown_max * 64 * cpl] (b <= kFastMaxB) | region, where region holds
+// this workgroup's rows of G (when a.preload) during the recurrence and the
+// update's reduction scratch afterwards.
+// Whole-CU LDS per workgroup keeps other kernels' workgroups off the CUs that
+// run the recurrence, whose inner steps are latency-bound.
+constexpr size_t kLdsBudget = 160 * 1024 - 256;
+constexpr size_t kLdsReserve = 136 * 1024;
+// Explicit address spaces keep the two sources of a G element from being
+// merged into one generic (flat) load.
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(1))) float global_f32;
+constexpr int kFastMaxB = 256;  // per-lane accumulators: up to 4 columns per lane
+constexpr int kMaxCpl = kFastMaxB / 64;
+constexpr int kMaxOwn = 4;      // own rows per minibatch on the fast path
+
+// Columns per lane of the fast-path variant chain_body runs for nown_max own
+// rows and cpl = ceil(b / 64) columns per lane (also the accumulators' pitch
+// in units of 64 floats).
+__host__ __device__ inline int fast_cols(int64_t nown_max, int64_t cpl) {
+  return (nown_max == 1 && cpl == 1) ? 1 : (nown_max <= 2 && cpl <= 2) ? 2 : kMaxCpl;
+}
+
 struct ChainLayout {
-  int64_t rs, vown, yown, region, region_len, total;
+  int64_t rs, vown, yown, acc, acc_len, region, region_len, total;
 };
 
 __host__ __device__ inline ChainLayout chain_layout(int s, int b, int Q, bool preload) {
   ChainLayout L;
   const int64_t sb = static_cast<int64_t>(s) * b;
   const int64_t nown_max = (b + Q - 1) / Q;
+  const int64_t cpl = fast_cols(nown_max, (b + 63) / 64);
   L.rs = 0;
   L.vown = (sb + 3) & ~3LL;
   L.yown = L.vown + ((s * nown_max + 3) & ~3LL);
-  L.region = L.yown + ((s * nown_max + 3) & ~3LL);
+  L.acc = L.yown + ((s * nown_max + 3) & ~3LL);
+  // the fast path needs its accumulators next to the update scratch
+  const int64_t acc_len = s * nown_max * 64 * cpl;
+  const bool fits = (L.acc + acc_len + 2048) * 4 <= static_cast<int64_t>(kLdsBudget);
+  L.acc_len = (b <= kFastMaxB && nown_max <= kMaxOwn && fits) ? acc_len : 0;
+  L.region = L.acc + L.acc_len;
   const int64_t gl = preload ? nown_max * b * (static_cast<int64_t>(s) * (s - 1) / 2) : 0;
   L.region_len = gl > 2048 ? gl : 2048;
   L.total = L.region + L.region_len;
   return L;
 }
 
-template <typename T, int LOSS>
-__global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float sm[];
-  const int s = a.s, b = a.b, Q = a.Q;
-  const int sb = s * b;
-  const int q = blockIdx.x;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int nown = (b - q + Q - 1) / Q;  // rows q, q+Q, ... below b
-  const ChainLayout L = chain_layout(s, b, Q, a.preload);
-  float* rs = sm + L.rs;      // r of all rows done so far
-  float* vown = sm + L.vown;  // margins of the own rows
-  float* yown = sm + L.yown;  // labels / targets of the own rows
-  float* gl = sm + L.region;  // own rows of G, then update scratch
-  __shared__ int abort_flag;
-  if (threadIdx.x == 0) abort_flag = 0;
-
-  const T* Y = static_cast<const T*>(a.Y);
-  const int64_t P = static_cast<int64_t>(b) * (static_cast<int64_t>(s) * (s - 1) / 2);
-
-  // ---- this workgroup's rows of every block-row of G into LDS, 16 loads in
-  // flight per lane.  Float4 f of own row t covers block-row j, columns
-  // 4k..4k+3 with f - t*P/4 = (b/4) j(j-1)/2 + k; its LDS slot is f itself.
-  if (a.preload) {
-    const int64_t P4 = P / 4;
-    const int64_t T4 = nown * P4;
-    const int b4 = b / 4;
-    const f32x4* G4 = reinterpret_cast<const f32x4*>(a.G);
-    f32x4* gl4 = reinterpret_cast<f32x4*>(gl);
-    for (int64_t f0 = threadIdx.x; f0 < T4; f0 += kThreads * 16) {
-      f32x4 tmp[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int64_t f = f0 + static_cast<int64_t>(kThreads) * u;
-        tmp[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (f < T4) {
-          const int t = static_cast<int>(f / P4);
-          const int64_t fr = f - t * P4;
-          const int64_t chunk = fr / b4;  // = j(j-1)/2 + k/b4
-          int j, kb;
-          block_of(static_cast<int>(chunk), j, kb);
-          const int64_t k4 = fr - static_cast<int64_t>(b4) * (static_cast<int64_t>(j) * (j - 1) / 2);
-          const int64_t i = q + static_cast<int64_t>(Q) * t;
-          tmp[u] = G4[(static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2) +
-                       i * j * b) / 4 + k4];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int64_t f = f0 + static_cast<int64_t>(kThreads) * u;
-        if (f < T4) gl4[f] = tmp[u];
-      }
+// Spin (bounded) until the LDS word *flag reaches `want` or the workgroup
+// aborts; false on abort or expiry.
+__device__ __forceinline__ bool lds_wait(const int* flag, int want, int* abort_flag, int* status) {
+  long it = 0;
+  while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < want) {
+    if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
+    if (++it > kSpinLimit) {
+      *abort_flag = 1;
+      atomicOr(status, 1);
+      return false;
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  return true;
+}
 
-  // ---- margins of the own rows (row p = (j, t) is minibatch j's row q + Q t)
-  chain::margins<T>(
-      Y, a.ld, a.n, a.w, s * nown,
-      [&](int p) {
-        const int j = p / nown;
-        return static_cast<int64_t>(j) * b + q + static_cast<int64_t>(Q) * (p - j * nown);
-      },
-      [&](int p, int64_t row, float v) {
-        vown[p] = v;
-        yown[p] = a.yB[row];
-        a.v[row] = v;
-      },
-      wave, lane);
-  __syncthreads();  // vown and the G rows ready
+// Publish `v` to the LDS word *flag after this wave's earlier LDS writes
+// (an LDS-only release: global stores in flight are not waited for).
+__device__ __forceinline__ void lds_publish(int* flag, int v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
-  // ---- inner recurrence.  Waves 1..3 compute and publish the own rows;
-  // wave 0 only polls for the step's r values, so its waits never queue
-  // behind another wave's memory traffic.
-  const bool vec = (b & 3) == 0;  // G rows are float4-aligned
-  for (int j = 0; j < s; ++j) {
-    const int jb = j * b;
-    if (wave > 0) {
-      const float* Gj = a.G + static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
-      for (int t = wave - 1; t < nown; t += kWaves - 1) {
-        const int i = q + Q * t;
-        float acc = 0.f;
-        if (a.preload) {
-          const f32x4* g4 = reinterpret_cast<const f32x4*>(gl + t * P + static_cast<int64_t>(b) * (static_cast<int64_t>(j) * (j - 1) / 2));
-          const f32x4* r4 = reinterpret_cast<const f32x4*>(rs);
-          for (int k4 = lane; k4 < (jb >> 2); k4 += 64) {
-            const f32x4 g = g4[k4];
-            const f32x4 rr = r4[k4];
-            acc = fmaf(g.x, rr.x, acc);
-            acc = fmaf(g.y, rr.y, acc);
-            acc = fmaf(g.z, rr.z, acc);
-            acc = fmaf(g.w, rr.w, acc);
-          }
-        } else if (vec) {
-          const f32x4* g4 = reinterpret_cast<const f32x4*>(Gj + static_cast<int64_t>(i) * jb);
-          const f32x4* r4 = reinterpret_cast<const f32x4*>(rs);
-          const int n4 = jb >> 2;
-          for (int k0 = lane; k0 < n4; k0 += 64 * 8) {
-            f32x4 g[8];
+// Everything a fast-path recurrence needs from chain_body.
+struct FastCtx {
+  const ChainArgs* a;
+  int q, nown, nown_max, lane, wave;
+  float *rs, *vown, *yown, *acc, *gl;
+  int64_t P;
+  int *abort_flag, *r_ready, *acc_ready;
+  const unsigned long long* mbox;
+};
+
+// Inner recurrence, fast path, for at most NO own rows per minibatch and CP
+// columns per lane (b <= 64 CP).  Wave 0 alone is on the critical
+// path: it collects r of block j-1 from its mailbox (lane l holds columns
+// l, l+64, ...), finishes z of its rows of block j with the one block
+// G_{j,j-1} on top of the per-lane partial sums, reduces once, and
+// publishes r.  Waves 1..3 fold each block t of r into the per-lane
+// partial sums of the rows of blocks k >= t+2 while wave 0 waits for the
+// next block, so z_j = v_j - c * sum_lanes(acc_j + G_{j,j-1} r_{j-1}).
+template <int LOSS, int NO, int CP>
+__device__ __forceinline__ void recurrence_fast(const FastCtx& x) {
+  const ChainArgs& a = *x.a;
+  const int s = a.s, b = a.b, Q = a.Q, sb = s * b;
+  const int q = x.q, nown = x.nown, nown_max = x.nown_max, lane = x.lane;
+  float* rs = x.rs;
+  const float* vown = x.vown;
+  const float* yown = x.yown;
+  float* acc = x.acc;
+  int& abort_flag = *x.abort_flag;
+  int& r_ready = *x.r_ready;
+  int* acc_ready = x.acc_ready;
+  const unsigned long long* mbox = x.mbox;
+  auto gval = [&](int k, int t, int col) -> float {
+    const int64_t tri = static_cast<int64_t>(k) * (k - 1) / 2;
+    if (a.preload) return ((const lds_f32*)x.gl)[t * x.P + static_cast<int64_t>(b) * tri + col];
+    const int64_t i = q + static_cast<int64_t>(Q) * t;
+    return ((const global_f32*)a.G)[static_cast<int64_t>(b) * b * tri + i * k * b + col];
+  };
+  const int wave = x.wave;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
+  constexpr int LWc = 64 * CP;  // acc row pitch
+  if (wv == 0) {
+    float rp[CP];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int k4 = k0 + 64 * u;
-              g[u] = k4 < n4 ? g4[k4] : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+    for (int u = 0; u < CP; ++u) rp[u] = 0.f;
+    for (int j = 0; j < s; ++j) {
+      const int jb = j * b;
+      // everything of step j that does not depend on r of block j-1 is
+      // read before the wait: G_{j,j-1} of the own rows, their margins and
+      // labels, and their partial sums if the helper has finished them
+      float gv[NO][CP], av[NO][CP], vj[NO], yj[NO];
+      const int* ready = &acc_ready[j % (kWaves - 1)];
+      const bool acc_now = j < 2 || __hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= j - 1;
+      if (acc_now) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int k4 = k0 + 64 * u;
-              if (k4 < n4) {
-                const f32x4 rr = r4[k4];
-                acc = fmaf(g[u].x, rr.x, acc);
-                acc = fmaf(g[u].y, rr.y, acc);
-                acc = fmaf(g[u].z, rr.z, acc);
-                acc = fmaf(g[u].w, rr.w, acc);
-              }
-            }
-          }
-        } else {
-          const float* grow = Gj + static_cast<int64_t>(i) * jb;
-          for (int k = lane; k < jb; k += 64) acc = fmaf(grow[k], rs[k], acc);
+      for (int t = 0; t < NO; ++t) {
+        vj[t] = t < nown ? vown[j * nown_max + t] : 0.f;
+        yj[t] = t < nown ? yown[j * nown_max + t] : 0.f;
+#pragma unroll
+        for (int u = 0; u < CP; ++u) {
+          const int l = lane + 64 * u;
+          const bool on = j > 0 && t < nown && l < b;
+          gv[t][u] = on ? gval(j, t, (j - 1) * b + l) : 0.f;
+          av[t][u] = (on && acc_now) ? acc[(j * nown_max + t) * LWc + l] : 0.f;
         }
-        acc = group_sum<64>(acc);  // every lane holds the sum
+      }
+      if (j > 0) {
+#pragma unroll
+        for (int u = 0; u < CP; ++u) {
+          const int l = lane + 64 * u;
+          if (l < b) {
+            rp[u] = chain::take(&mbox[jb - b + l], a.epoch, a.status, &abort_flag, 0);
+            rs[jb - b + l] = rp[u];
+          }
+        }
+        if (abort_flag) break;
+        lds_publish(&r_ready, j);
+        if (!acc_now) {
+          if (!lds_wait(ready, j - 1, &abort_flag, a.status)) break;
+#pragma unroll
+          for (int t = 0; t < NO; ++t)
+#pragma unroll
+            for (int u = 0; u < CP; ++u) {
+              const int l = lane + 64 * u;
+              if (t < nown && l < b) av[t][u] = acc[(j * nown_max + t) * LWc + l];
+            }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NO; ++t) {
+        if (t >= nown) break;
+        const int i = q + Q * t;
+        float part = 0.f;
+#pragma unroll
+        for (int u = 0; u < CP; ++u)
+          part += fmaf(gv[t][u], rp[u], av[t][u]);
+        const float tot = wave_sum(part);
         const int64_t row = jb + i;
-        const float zz = vown[j * nown + t] - a.c * acc;
-        const float rv = loss_deriv<LOSS>(zz, yown[j * nown + t]);
+        const float zz = vj[t] - a.c * tot;
+        const float rv = loss_deriv<LOSS>(zz, yj[t]);
         const uint64_t word = tagged(a.epoch, rv);
-        // one copy per reader: each workgroup polls only its own mailbox
-        for (int dst = lane; dst < Q; dst += 64)
-          __hip_atomic_store(&a.xbuf[static_cast<int64_t>(dst) * sb + row], word, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        for (int dst = lane; dst < Q; dst += 64) chain::put(&a.xbuf[static_cast<int64_t>(dst) * sb + row], word);
         if (lane == 0) {
           a.z[row] = zz;
           a.r[row] = rv;
         }
       }
-    } else {
-      // collect r_j of every row from this workgroup's mailbox
-      const unsigned long long* mbox = a.xbuf + static_cast<int64_t>(q) * sb;
-      for (int k = lane; k < b; k += 64) {
-        uint64_t x = 0;
-        long it = 0;
-        while (true) {
-          x = __hip_atomic_load(&mbox[jb + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (static_cast<uint32_t>(x >> 32) == a.epoch) break;
-          if (++it > kSpinLimit) {
-            abort_flag = 1;
-            atomicOr(a.status, 1);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        rs[jb + k] = __uint_as_float(static_cast<uint32_t>(x));
-      }
     }
+    // the last block's r, for the update
+    if (!abort_flag) {
+      const int jb = (s - 1) * b;
+      for (int l = lane; l < b; l += 64) rs[jb + l] = chain::take(&mbox[jb + l], a.epoch, a.status, &abort_flag, 0);
+    }
+  } else {
+    // helper wv - 1 owns the rows of the blocks k = wv - 1 (mod 3); after r
+    // of block tb is in, it folds G_{k,tb} r_tb into their partial sums for
+    // every k >= tb + 2, two blocks at a time with all loads issued first
+    const int h = wv - 1;
+    for (int tb = 0; tb + 2 < s; ++tb) {
+      if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status)) break;
+      float rr[CP];
+#pragma unroll
+      for (int u = 0; u < CP; ++u) {
+        const int l = lane + 64 * u;
+        rr[u] = (l < b) ? rs[tb * b + l] : 0.f;
+      }
+      int k0 = tb + 2;
+      k0 += (h - k0 % (kWaves - 1) + (kWaves - 1)) % (kWaves - 1);  // first k >= tb+2 with k = h (mod 3)
+      for (int k = k0; k < s; k += 2 * (kWaves - 1)) {
+        float gb[2][NO][CP], ab[2][NO][CP];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int kk = k + e * (kWaves - 1);
+#pragma unroll
+          for (int t = 0; t < NO; ++t)
+#pragma unroll
+            for (int u = 0; u < CP; ++u) {
+              const int l = lane + 64 * u;
+              const bool on = kk < s && t < nown && l < b;
+              gb[e][t][u] = on ? gval(kk, t, tb * b + l) : 0.f;
+              ab[e][t][u] = on ? acc[(kk * nown_max + t) * LWc + l] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int kk = k + e * (kWaves - 1);
+#pragma unroll
+          for (int t = 0; t < NO; ++t)
+#pragma unroll
+            for (int u = 0; u < CP; ++u) {
+              const int l = lane + 64 * u;
+              if (kk < s && t < nown && l < b)
+                acc[(kk * nown_max + t) * LWc + l] = fmaf(gb[e][t][u], rr[u], ab[e][t][u]);
+            }
+        }
+      }
+      lds_publish(&acc_ready[h], tb + 1);
+    }
+  }
+}
+
+// The work of workgroup q (0 <= q < a.Q); called by all 256 lanes.
+template <typename T, int LOSS>
+__device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  const int s = a.s, b = a.b, Q = a.Q;
+  const int sb = s * b;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nown = (b - q + Q - 1) / Q;  // rows q, q+Q, ... below b
+  const int nown_max = (b + Q - 1) / Q;
+  const ChainLayout L = chain_layout(s, b, Q, a.preload);
+  const bool fast = L.acc_len > 0;
+  const int cpl = (b + 63) / 64;
+  float* rs = sm + L.rs;      // r of all rows done so far
+  float* vown = sm + L.vown;  // margins of the own rows
+  float* yown = sm + L.yown;  // labels / targets of the own rows
+  float* acc = sm + L.acc;    // per-lane partial sums of the own rows (fast path)
+  float* gl = sm + L.region;  // own rows of G, then update scratch
+  __shared__ int abort_flag;
+  __shared__ int r_ready;                  // blocks whose r is in rs (wave 0)
+  __shared__ int acc_ready[kWaves - 1];    // blocks folded into acc (waves 1..3)
+  if (threadIdx.x == 0) {
+    abort_flag = 0;
+    r_ready = 0;
+    for (int k = 0; k < kWaves - 1; ++k) acc_ready[k] = 0;
+  }
+  for (int64_t k = threadIdx.x; k < L.acc_len; k += kThreads) acc[k] = 0.f;
+
+  const T* Y = static_cast<const T*>(a.Y);
+  const int64_t P = static_cast<int64_t>(b) * (static_cast<int64_t>(s) * (s - 1) / 2);
+
+  // ---- this workgroup's rows of every block-row of G go to LDS, 16 loads in
+  // flight per lane; the first batch is issued before the margins so both
+  // wait on memory together.  Own row t of block-row j is a contiguous run of
+  // j*b/4 float4 in G and in LDS (at t*P/4 + (b/4) j(j-1)/2).  Slots
+  // enumerate (t, j, c4) on power-of-two strides so a slot decodes with
+  // shifts; slots past a run's end are skipped.
+  const int64_t P4 = P / 4;
+  const int b4 = b / 4;
+  int lgW = 0, lgJ = 0;
+  while ((1 << lgW) < (s - 1) * b4) ++lgW;
+  while ((1 << lgJ) < s - 1) ++lgJ;
+  const int64_t T4 = (a.preload && s > 1) ? static_cast<int64_t>(nown) << (lgW + lgJ) : 0;
+  const f32x4* G4 = reinterpret_cast<const f32x4*>(a.G);
+  f32x4* gl4 = reinterpret_cast<f32x4*>(gl);
+  auto slot = [&](int64_t g, int64_t& src, int64_t& dst) -> bool {
+    const int c4 = static_cast<int>(g & ((1 << lgW) - 1));
+    const int j = 1 + static_cast<int>((g >> lgW) & ((1 << lgJ) - 1));
+    const int t = static_cast<int>(g >> (lgW + lgJ));
+    if (g >= T4 || j >= s || c4 >= j * b4) return false;
+    const int64_t tri = static_cast<int64_t>(j) * (j - 1) / 2;
+    const int64_t i = q + static_cast<int64_t>(Q) * t;
+    src = (static_cast<int64_t>(b) * b * tri + i * j * b) / 4 + c4;
+    dst = t * P4 + b4 * tri + c4;
+    return true;
+  };
+  auto g_issue = [&](f32x4 (&tmp)[16], int64_t g0) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      int64_t src = 0, dst = 0;
+      slot(g0 + static_cast<int64_t>(kThreads) * u, src, dst);
+      tmp[u] = G4[src];  // skipped slots read G's first float4
+    }
+  };
+  auto g_store = [&](const f32x4 (&tmp)[16], int64_t g0) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      int64_t src = 0, dst = 0;
+      if (slot(g0 + static_cast<int64_t>(kThreads) * u, src, dst)) gl4[dst] = tmp[u];
+    }
+  };
+  {
+    f32x4 tmp[16];
+    if (T4 > 0) g_issue(tmp, threadIdx.x);
+    // ---- margins of the own rows (row p = (j, t) is minibatch j's row q + Q t)
+    chain::margins<T>(
+        Y, a.ld, a.n, a.w, s * nown,
+        [&](int p) {
+          const int j = p / nown;
+          return static_cast<int64_t>(j) * b + q + static_cast<int64_t>(Q) * (p - j * nown);
+        },
+        [&](int p, int64_t row, float v) {
+          const int j = p / nown;
+          vown[j * nown_max + (p - j * nown)] = v;
+          yown[j * nown_max + (p - j * nown)] = a.yB[row];
+          a.v[row] = v;
+        },
+        wave, lane);
+    if (T4 > 0) g_store(tmp, threadIdx.x);
+    for (int64_t f0 = threadIdx.x + kThreads * 16; f0 < T4; f0 += kThreads * 16) {
+      g_issue(tmp, f0);
+      g_store(tmp, f0);
+    }
+  }
+  __syncthreads();  // vown, acc, flags and the G rows ready
+
+
+  const unsigned long long* mbox = a.xbuf + static_cast<int64_t>(q) * sb;
+
+  if (fast) {
+    FastCtx x{&a, q, nown, nown_max, lane, wave, rs, vown, yown, acc, gl, P, &abort_flag, &r_ready, acc_ready, mbox};
+    const int fc = fast_cols(nown_max, cpl);
+    if (fc == 1) recurrence_fast<LOSS, 1, 1>(x);
+    else if (fc == 2) recurrence_fast<LOSS, 2, 2>(x);
+    else recurrence_fast<LOSS, kMaxOwn, kMaxCpl>(x);
     __syncthreads();
     if (abort_flag) return;
+  } else {
+    // ---- inner recurrence, any b.  Waves 1..3 compute and publish the own rows;
+    // wave 0 only polls for the step's r values, so its waits never queue
+    // behind another wave's memory traffic.
+    const bool vec = (b & 3) == 0;  // G rows are float4-aligned
+    for (int j = 0; j < s; ++j) {
+      const int jb = j * b;
+      if (wave > 0) {
+        const float* Gj = a.G + static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
+        for (int t = wave - 1; t < nown; t += kWaves - 1) {
+          const int i = q + Q * t;
+          float dot = 0.f;
+          if (a.preload) {
+            const f32x4* g4 = reinterpret_cast<const f32x4*>(gl + t * P + static_cast<int64_t>(b) * (static_cast<int64_t>(j) * (j - 1) / 2));
+            const f32x4* r4 = reinterpret_cast<const f32x4*>(rs);
+            for (int k4 = lane; k4 < (jb >> 2); k4 += 64) {
+              const f32x4 g = g4[k4];
+              const f32x4 rr = r4[k4];
+              dot = fmaf(g.x, rr.x, dot);
+              dot = fmaf(g.y, rr.y, dot);
+              dot = fmaf(g.z, rr.z, dot);
+              dot = fmaf(g.w, rr.w, dot);
+            }
+          } else if (vec) {
+            const f32x4* g4 = reinterpret_cast<const f32x4*>(Gj + static_cast<int64_t>(i) * jb);
+            const f32x4* r4 = reinterpret_cast<const f32x4*>(rs);
+            const int n4 = jb >> 2;
+            for (int k0 = lane; k0 < n4; k0 += 64 * 8) {
+              f32x4 g[8];
+  #pragma unroll
+              for (int u = 0; u < 8; ++u) {
+                const int k4 = k0 + 64 * u;
+                g[u] = k4 < n4 ? g4[k4] : f32x4{0.f, 0.f, 0.f, 0.f};
+              }
+  #pragma unroll
+              for (int u = 0; u < 8; ++u) {
+                const int k4 = k0 + 64 * u;
+                if (k4 < n4) {
+                  const f32x4 rr = r4[k4];
+                  dot = fmaf(g[u].x, rr.x, dot);
+                  dot = fmaf(g[u].y, rr.y, dot);
+                  dot = fmaf(g[u].z, rr.z, dot);
+                  dot = fmaf(g[u].w, rr.w, dot);
+                }
+              }
+            }
+          } else {
+            const float* grow = Gj + static_cast<int64_t>(i) * jb;
+            for (int k = lane; k < jb; k += 64) dot = fmaf(grow[k], rs[k], dot);
+          }
+          dot = group_sum<64>(dot);  // every lane holds the sum
+          const int64_t row = jb + i;
+          const float zz = vown[j * nown_max + t] - a.c * dot;
+          const float rv = loss_deriv<LOSS>(zz, yown[j * nown_max + t]);
+          const uint64_t word = tagged(a.epoch, rv);
+          // one copy per reader: each workgroup polls only its own mailbox
+          for (int dst = lane; dst < Q; dst += 64)
+            __hip_atomic_store(&a.xbuf[static_cast<int64_t>(dst) * sb + row], word, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          if (lane == 0) {
+            a.z[row] = zz;
+            a.r[row] = rv;
+          }
+        }
+      } else {
+        // collect r_j of every row from this workgroup's mailbox
+        for (int k = lane; k < b; k += 64) {
+          uint64_t x = 0;
+          long it = 0;
+          while (true) {
+            x = __hip_atomic_load(&mbox[jb + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (static_cast<uint32_t>(x >> 32) == a.epoch) break;
+            if (++it > kSpinLimit) {
+              abort_flag = 1;
+              atomicOr(a.status, 1);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          rs[jb + k] = __uint_as_float(static_cast<uint32_t>(x));
+        }
+      }
+      __syncthreads();
+      if (abort_flag) return;
+    }
   }
 
   // ---- update of this workgroup's columns of w; the G rows are no longer needed
   chain::update_columns<T>(Y, a.ld, a.n, sb, rs, a.c, a.w, q, Q, gl);
+}
+
+template <typename T, int LOSS>
+__global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
+  chain_body<T, LOSS>(a, blockIdx.x);
+}
+
+// One launch of the pipelined training loop: the recurrence of outer step k
+// (workgroups [0, Q)), the Gram of step k+1 and the gather of step k+2, each
+// on buffers no other role of the launch touches, so the three need no
+// synchronisation with each other; stream order between consecutive launches
+// supplies every dependence.
+template <int GS>
+__device__ __forceinline__ void pipe_gather(const PipeArgs& p, int g) {
+  constexpr int RPW = kThreads / GS;  // rows per workgroup pass
+  for (int row0 = g * RPW; row0 < p.sb; row0 += p.gath_wgs * RPW)
+    gather::copy_row<GS>(static_cast<const u32x4*>(p.Xs), p.y, p.m, p.cpr, p.sb, p.seed, nullptr,
+                         p.idx_out, static_cast<u32x4*>(p.Yo), p.yBo,
+                         row0 + static_cast<int>(threadIdx.x) / GS, threadIdx.x % GS);
+}
+
+template <int LOSS, int BK, int D>
+__global__ __launch_bounds__(kThreads) void pipe_kernel(PipeArgs p) {
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  const int w = blockIdx.x;
+  if (w < p.a.Q) {
+    chain_body<uint16_t, LOSS>(p.a, w);
+    return;
+  }
+  if (w >= p.gram0 && w < p.gram0 + p.gram_slots) {
+    const int tile = p.order[w - p.gram0];
+    if (tile >= 0)
+      gram::bf16_tile<BK, D>(p.gY, p.a.ld, p.a.b, p.tps, p.gG, tile, reinterpret_cast<uint16_t*>(sm));
+    return;
+  }
+  if (w >= p.gath0 && w < p.gath0 + p.gath_wgs) {
+    const int g = w - p.gath0;
+    switch (p.gs) {
+      case 64: pipe_gather<64>(p, g); break;
+      case 32: pipe_gather<32>(p, g); break;
+      case 16: pipe_gather<16>(p, g); break;
+      case 8: pipe_gather<8>(p, g); break;
+      default: pipe_gather<4>(p, g); break;
+    }
+  }
+}
+
+template <int LOSS, int BK, int D>
+hipError_t pipe_t(const PipeArgs& p, int grid, size_t lds, hipStream_t st, const LaunchTimer& tm) {
+  static size_t granted = 64 * 1024;
+  if (lds > granted) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pipe_kernel<LOSS, BK, D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    granted = lds;
+  }
+  return launch_kernel(pipe_kernel<LOSS, BK, D>, dim3(grid), dim3(kThreads), lds, st, tm, p);
+}
+
+template <int LOSS>
+hipError_t pipe_l(const PipeArgs& p, int grid, size_t lds, hipStream_t st, const LaunchTimer& tm) {
+  switch (gram_variant(p.a.ld)) {
+    case 0: return pipe_t<LOSS, 32, 1>(p, grid, lds, st, tm);
+    case 1: return pipe_t<LOSS, 64, 8>(p, grid, lds, st, tm);
+    case 2: return pipe_t<LOSS, 64, 4>(p, grid, lds, st, tm);
+    default: return pipe_t<LOSS, 64, 2>(p, grid, lds, st, tm);
+  }
 }
 
 template <typename T, int LOSS>
@@ -227,11 +543,6 @@ hipError_t chain_t(const ChainArgs& a, size_t lds, hipStream_t st, const LaunchT
 }
 
 }  // namespace
-
-// Whole-CU LDS per workgroup keeps other kernels' workgroups off the CUs that
-// run the recurrence, whose inner steps are latency-bound.
-constexpr size_t kLdsBudget = 160 * 1024 - 256;
-constexpr size_t kLdsReserve = 136 * 1024;
 
 bool chain_preload(int s, int b, int Q) {
   if ((b & 3) != 0) return false;
@@ -261,6 +572,18 @@ hipError_t launch_chain(int storage, int loss, const ChainArgs& a_in, hipStream_
   if (loss == kLogistic) return chain_t<float, kLogistic>(a, lds, st, tm);
   if (loss == kSquared) return chain_t<float, kSquared>(a, lds, st, tm);
   return chain_t<float, kPoisson>(a, lds, st, tm);
+}
+
+hipError_t launch_pipe(int loss, const PipeArgs& p_in, hipStream_t st, const LaunchTimer& tm) {
+  PipeArgs p = p_in;
+  p.a.preload = chain_preload(p.a.s, p.a.b, p.a.Q) ? 1 : 0;
+  size_t lds = chain_lds_bytes(p.a.s, p.a.b, p.a.Q);
+  const size_t glds = sizeof(uint16_t) * (gram_variant(p.a.ld) == 0 ? gram::lds_elems<32>() : gram::lds_elems<64>());
+  if (glds > lds) lds = glds;
+  const int grid = p.gath_wgs > 0 ? p.gath0 + p.gath_wgs : (p.gram_slots > 0 ? p.gram0 + p.gram_slots : p.a.Q);
+  if (loss == kLogistic) return pipe_l<kLogistic>(p, grid, lds, st, tm);
+  if (loss == kSquared) return pipe_l<kSquared>(p, grid, lds, st, tm);
+  return pipe_l<kPoisson>(p, grid, lds, st, tm);
 }
 
 }  // namespace casgd

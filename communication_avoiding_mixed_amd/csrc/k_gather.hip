@@ -4,6 +4,7 @@
 // prescribes; rows are padded to ld (a multiple of 32 elements) so every row
 // is a whole number of 16-byte chunks.
 #include "casgd_device.h"
+#include "casgd_gather.h"
 #include "casgd_internal.h"
 
 namespace casgd {
@@ -53,44 +54,15 @@ __global__ __launch_bounds__(256) void store_f32_kernel(const float* __restrict_
   }
 }
 
-// ---------------------------------------------------------------------------
-// Sample + gather.  A group of GS lanes copies one row of Y with 16-byte
-// loads and stores (GS chosen so the group spans the row's chunks); each lane
-// issues all of its loads of a row before its stores, so a row costs one
-// memory round trip.
-// ---------------------------------------------------------------------------
+// Sample + gather: one workgroup of 256 lanes copies 256/GS rows (the row
+// copy itself is in casgd_gather.h).
 template <int GS>
 __global__ __launch_bounds__(256) void gather_kernel(
     const u32x4* __restrict__ Xs, const float* __restrict__ y, int64_t m, int64_t cpr, int sb,
     uint64_t seed, const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx_out,
     u32x4* __restrict__ Y, float* __restrict__ yB) {
-  constexpr int U = 4;
-  const int lane = threadIdx.x % GS;
   const int row = blockIdx.x * (256 / GS) + threadIdx.x / GS;
-  if (row >= sb) return;  // whole lane groups leave together
-  int64_t src = idx_in ? static_cast<int64_t>(idx_in[row])
-                       : static_cast<int64_t>(sample_row(seed, static_cast<uint64_t>(row),
-                                                         static_cast<uint64_t>(m)));
-  src = src < 0 ? 0 : (src >= m ? m - 1 : src);  // explicit indices are checked on the host
-  if (lane == 0) {
-    idx_out[row] = static_cast<int32_t>(src);
-    yB[row] = y[src];
-  }
-  const u32x4* xr = Xs + src * cpr;
-  u32x4* yr = Y + static_cast<int64_t>(row) * cpr;
-  for (int64_t c0 = lane; c0 < cpr; c0 += GS * U) {
-    u32x4 q[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + GS * u;
-      q[u] = c < cpr ? xr[c] : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + GS * u;
-      if (c < cpr) yr[c] = q[u];
-    }
-  }
+  gather::copy_row<GS>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, row, threadIdx.x % GS);
 }
 
 template <int GS>

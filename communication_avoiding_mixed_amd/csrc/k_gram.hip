@@ -4,149 +4,28 @@
 // Linear Models on GPUs" forms the sb x sb Gram from low-precision inputs with
 // high-precision accumulation on the GPU's matrix hardware; the inner
 // recurrence only ever reads blocks G_{j,t} with t < j, so only those are
-// computed.  On gfx950 this is bf16 MFMA (v_mfma_f32_32x32x16_bf16) with
-// float32 accumulators.  Both operands are rows of Y (an "NT" product), so
-// A and B tiles are staged through LDS the same way.
-//
-// Output layout (block-row): block-row j (1 <= j < s) is the b x (j*b)
-// row-major matrix [G_{j,0} ... G_{j,j-1}] starting at element b*b*j*(j-1)/2.
+// computed.  bf16 storage uses the MFMA tile of casgd_gram.h; float32 storage
+// runs the same tiles on the vector ALUs.
 #include "casgd_device.h"
+#include "casgd_gram.h"
 #include "casgd_internal.h"
 
 namespace casgd {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+using gram::kTile;
 
-constexpr int kTile = 64;  // output tile edge; 4 waves of 32 x 32
-
-// One 64 x 64 output tile per workgroup of 256 lanes; blockIdx.x enumerates
-// (block (j,t), tile row, tile col).  Output rows and columns past the block
-// edge (b not a multiple of 64) are not stored.  K is walked in BK-wide
-// stages: each stage's global loads are issued D stages before it is used
-// (a ring of D register sets per lane), then the stage is copied into one of
-// two LDS buffers and consumed by the MFMAs.  Loads carry no branches and
-// their data is not touched until the LDS copy, so the compiler waits for
-// exactly the stage it needs and D stages stay in flight.  The stage count
-// is padded to a multiple of D with zero stages.
+// One 64 x 64 output tile per workgroup; `order` maps workgroups to tiles
+// (XCD-grouped) and holds -1 for the workgroups that pad the grid.
 template <int BK, int D>
 __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restrict__ Y,
                                                         int64_t ld, int b, int tps,
                                                         float* __restrict__ G,
                                                         const int* __restrict__ order) {
-  constexpr int CPR = BK / 8;          // 16-byte chunks per tile row per stage
-  constexpr int RPP = 256 / CPR;       // tile rows loaded per pass
-  constexpr int PASSES = kTile / RPP;  // passes per operand per stage
-  constexpr int LW = BK + 8;           // LDS row pitch (elements), breaks bank aliasing
-
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kTile * LW];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * LW];
-
-  const int nt2 = tps * tps;
-  const int tile = order[blockIdx.x];  // XCD-grouped tile order; -1 pads the grid
+  __shared__ __attribute__((aligned(16))) uint16_t lds[gram::lds_elems<BK>()];
+  const int tile = order[blockIdx.x];
   if (tile < 0) return;
-  const int p = tile / nt2;
-  const int rem = tile - p * nt2;
-  const int ti = rem / tps;
-  const int tj = rem - ti * tps;
-  int j, t;
-  block_of(p, j, t);
-
-  float* Gj = G + static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
-  const int64_t ldg = static_cast<int64_t>(j) * b;
-  const int a0 = ti * kTile;  // first row of the A tile inside block-row j
-  const int b0 = tj * kTile;  // first row of the B tile inside block-row t
-
-  // Rows past the block edge read rows of the same block instead; they only
-  // feed output rows / columns that are never stored.
-  const int lrow = threadIdx.x / CPR;
-  const int lchunk = threadIdx.x - lrow * CPR;
-  const uint16_t* aptr[PASSES];
-  const uint16_t* bptr[PASSES];
-#pragma unroll
-  for (int q = 0; q < PASSES; ++q) {
-    const int r = lrow + q * RPP;
-    const int ar = a0 + r < b ? r : 0;
-    const int br = b0 + r < b ? r : 0;
-    aptr[q] = Y + (static_cast<int64_t>(j) * b + a0 + ar) * ld + lchunk * 8;
-    bptr[q] = Y + (static_cast<int64_t>(t) * b + b0 + br) * ld + lchunk * 8;
-  }
-
-  // Chunks past the end of the row (a half-width last stage, or the zero
-  // stages that pad the count to a multiple of D) read column 0 and are
-  // zeroed when copied to LDS, D stages later, so no load waits early.
-  u32x4 ra[D][PASSES], rb[D][PASSES];
-  bool kin[D];
-  const int64_t nstage = (ld + BK - 1) / BK;
-  const int64_t nst_pad = (nstage + D - 1) / D * D;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  auto load_stage = [&](int slot, int64_t st) {
-    const int64_t k0 = st * BK;
-    kin[slot] = k0 + lchunk * 8 < ld;
-    const int64_t off = kin[slot] ? k0 : 0;
-#pragma unroll
-    for (int q = 0; q < PASSES; ++q) {
-      ra[slot][q] = *reinterpret_cast<const u32x4*>(aptr[q] + off);
-      rb[slot][q] = *reinterpret_cast<const u32x4*>(bptr[q] + off);
-    }
-  };
-
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int arow = wm * 32 + (lane & 31);
-  const int brow = wn * 32 + (lane & 31);
-  const int kofs = (lane >> 5) * 8;
-
-  // one accumulator per 16-wide K slice of a stage: the MFMAs of a stage are
-  // independent and issue back to back instead of waiting on each other
-  constexpr int NACC = BK / 16;
-  f32x16_t acc[NACC];
-#pragma unroll
-  for (int kk = 0; kk < NACC; ++kk)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[kk][e] = 0.f;
-
-#pragma unroll
-  for (int d = 0; d < D; ++d) load_stage(d, d);
-
-  for (int64_t st0 = 0; st0 < nst_pad; st0 += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int buf = static_cast<int>((st0 + d) & 1);
-#pragma unroll
-      for (int q = 0; q < PASSES; ++q) {
-        const int r = lrow + q * RPP;
-        *reinterpret_cast<u32x4*>(&As[buf][r * LW + lchunk * 8]) = kin[d] ? ra[d][q] : zero;
-        *reinterpret_cast<u32x4*>(&Bs[buf][r * LW + lchunk * 8]) = kin[d] ? rb[d][q] : zero;
-      }
-      __syncthreads();
-      load_stage(d, st0 + d + D);
-#pragma unroll
-      for (int kk = 0; kk < NACC; ++kk) {
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&As[buf][arow * LW + kk * 16 + kofs]);
-        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][brow * LW + kk * 16 + kofs]);
-        acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[kk], 0, 0, 0);
-      }
-    }
-  }
-#pragma unroll
-  for (int kk = 1; kk < NACC; ++kk)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[0][e] += acc[kk][e];
-
-  // Accumulator element e of lane l holds row 8*(e/4) + 4*(l/32) + e%4,
-  // column l%32 of the wave's 32 x 32 sub-tile.
-  const int col = b0 + wn * 32 + (lane & 31);
-  if (col < b) {
-    float* gcol = Gj + static_cast<int64_t>(t) * b + col;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = a0 + wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (row < b) gcol[row * ldg] = acc[0][e];
-    }
-  }
+  gram::bf16_tile<BK, D>(Y, ld, b, tps, G, tile, lds);
 }
 
 // float32 storage: the same tiles on the vector ALUs (each lane a 4 x 4
@@ -265,11 +144,12 @@ hipError_t launch_gram(int storage, const void* Y, int64_t ld, int s, int b, flo
   const dim3 grid(static_cast<unsigned>(plan.slots));
   if (storage == kStoreBF16) {
     const uint16_t* Yb = static_cast<const uint16_t*>(Y);
-    if (ld <= 32) return launch_kernel(gram_bf16_kernel<32, 1>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
-    const int64_t nstage = (ld + 63) / 64;
-    if (nstage >= 8) return launch_kernel(gram_bf16_kernel<64, 8>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
-    if (nstage >= 4) return launch_kernel(gram_bf16_kernel<64, 4>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
-    return launch_kernel(gram_bf16_kernel<64, 2>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
+    switch (gram_variant(ld)) {
+      case 0: return launch_kernel(gram_bf16_kernel<32, 1>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
+      case 1: return launch_kernel(gram_bf16_kernel<64, 8>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
+      case 2: return launch_kernel(gram_bf16_kernel<64, 4>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
+      default: return launch_kernel(gram_bf16_kernel<64, 2>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
+    }
   }
   return launch_kernel(gram_f32_kernel, grid, dim3(256), 0, st, tm, static_cast<const float*>(Y), ld, b,
                        tps, G, order);

@@ -68,7 +68,9 @@ enum casgd_kernel_id {
   CASGD_K_GATHER = 0, /* sample + gather of the s*b rows                        */
   CASGD_K_GRAM = 1,   /* strictly-lower Gram on bf16 MFMA                       */
   CASGD_K_CHAIN = 2,  /* margins + inner recurrence + weight update (one launch) */
-  CASGD_K_COUNT = 3
+  CASGD_K_PIPE = 3,   /* casgd_train's step launch: chain of step k, Gram of     */
+                      /* step k+1 and gather of step k+2 together               */
+  CASGD_K_COUNT = 4
 };
 
 /*
@@ -123,7 +125,13 @@ int casgd_outer_step_indices(casgd_handle h, int s, int b, float eta,
 /*
  * n_outer consecutive outer iterations; outer step k (k = first_step ...
  * first_step + n_outer - 1) samples with seed casgd_step_seed(base_seed, k).
- * Equivalent to calling casgd_outer_step with those seeds.  Asynchronous.
+ * Bit-identical to calling casgd_outer_step with those seeds.  Asynchronous.
+ * With bf16 storage and the default recurrence the loop is pipelined on the
+ * handle's stream alone: after a prologue (gather and Gram of the first step,
+ * gather of the second), each step is ONE launch that runs the margins,
+ * recurrence and update of step k next to the Gram of step k+1 and the
+ * gather of step k+2 (timer CASGD_K_PIPE).  Otherwise each step is queued as
+ * by casgd_outer_step.
  */
 int casgd_train(casgd_handle h, int s, int b, float eta, uint64_t base_seed,
                 uint64_t first_step, int n_outer, float* w);

@@ -212,8 +212,11 @@ def test_side_stream_and_timing():
         w = torch.zeros(wl.n, device="cuda")
         h.set_timing(True)
         h.train(wl.s, wl.b, wl.eta, 0, 0, 5, w)
-        ms, cnt = h.timing(B.K_GRAM)
+        ms, cnt = h.timing(B.K_PIPE)
+        g_ms, g_cnt = h.timing(B.K_GRAM)
         h.set_timing(False)
     side.synchronize()
     assert torch.equal(w, w_ref)
+    # pipelined: one stand-alone Gram (the first step's), then one launch per step
     assert cnt == 5 and ms > 0
+    assert g_cnt == 1 and g_ms > 0
