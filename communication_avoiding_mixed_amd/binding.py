@@ -206,8 +206,9 @@ class CASGD:
     def set_option(self, option: int, value: int):
         _check(load().casgd_set_option(self._handle(), option, value), "casgd_set_option")
 
-    def set_timing(self, on: bool):
-        _check(load().casgd_set_timing(self._handle(), 1 if on else 0), "casgd_set_timing")
+    def set_timing(self, on, every: int = 1):
+        """Stamp every `every`-th launch of each kernel (on), or stop (off)."""
+        _check(load().casgd_set_timing(self._handle(), int(every) if on else 0), "casgd_set_timing")
 
     def timing(self, kernel: int, reset: bool = False):
         ms = ctypes.c_double(0.0)

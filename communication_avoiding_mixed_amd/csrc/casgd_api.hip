@@ -84,7 +84,8 @@ struct casgd_ctx {
   int last_buf = 0;
   int last_s = 0, last_b = 0;
 
-  bool timing = false;
+  int timing = 0;  // 0 off, else stamp every timing-th launch of each kernel
+  int64_t issued[CASGD_K_COUNT] = {};
   std::vector<EventPair> pending[CASGD_K_COUNT];
   std::vector<EventPair> pool;
   double total_ms[CASGD_K_COUNT] = {};
@@ -201,7 +202,7 @@ EventPair take_pair(casgd_ctx* h) {
 // kernel's own dispatch (start and end of that kernel).
 template <typename Fn>
 hipError_t timed(casgd_ctx* h, int kernel, Fn&& fn) {
-  if (!h->timing) return fn(casgd::LaunchTimer{});
+  if (!h->timing || h->issued[kernel]++ % h->timing != 0) return fn(casgd::LaunchTimer{});
   EventPair p = take_pair(h);
   hipError_t e = fn(casgd::LaunchTimer{p.start, p.stop});
   h->pending[kernel].push_back(p);
@@ -611,7 +612,9 @@ int casgd_export_rows(casgd_handle h, int64_t row0, int64_t nrows, void* dst, si
 
 int casgd_set_timing(casgd_handle h, int on) {
   if (!h) return fail(CASGD_EINVAL, "NULL handle");
-  h->timing = on != 0;
+  if (on < 0) return fail(CASGD_EINVAL, "timing period must be >= 0");
+  h->timing = on;
+  for (auto& c : h->issued) c = 0;
   return CASGD_OK;
 }
 

@@ -67,57 +67,77 @@ __device__ __forceinline__ float take(const unsigned long long* p, uint32_t epoc
 }
 
 // Margins x . w of `nrows` rows of Y, row number row_of(p) for p < nrows.
-// Each wave takes kRB rows at a time so their loads are in flight together.
-// lane 0 of the wave calls out(p, row, value).
-template <typename T, typename RowOf, typename Out>
-__device__ __forceinline__ void margins(const T* Y, int64_t ld, int64_t n, const float* w, int nrows, RowOf row_of,
-                        Out out, int wave, int lane) {
+// Each wave takes kRB rows at a time so their loads are in flight together;
+// the weights of the same columns are loaded in the same batch.  `issued()`
+// runs once, right after the first batch's loads are issued and before any
+// of them is waited for, so a caller can put its own loads in flight beside
+// them.  lane 0 of the wave calls out(p, row, value).
+template <typename T, typename RowOf, typename Out, typename Issued>
+__device__ __forceinline__ void margins(const T* Y, int64_t ld, int64_t n, const float* w, int nrows,
+                                        RowOf row_of, Out out, int wave, int lane, Issued issued) {
   constexpr int E = Elems<T>::E;
   constexpr int kRB = 4;
   const int64_t cpr = ld / E;
   const bool w_vec = (reinterpret_cast<uintptr_t>(w) & 15) == 0;
-  for (int p0 = wave * kRB; p0 < nrows; p0 += kWaves * kRB) {
+  bool first = true;
+  // every wave makes the same number of passes, so `issued` runs in all of them
+  const int passes = (nrows + kWaves * kRB - 1) / (kWaves * kRB);
+  for (int pass = 0; pass < (passes > 0 ? passes : 1); ++pass) {
+    const int p0 = (pass * kWaves + wave) * kRB;
     float acc[kRB];
 #pragma unroll
     for (int r = 0; r < kRB; ++r) acc[r] = 0.f;
-    for (int64_t c0 = lane; c0 < cpr; c0 += 64 * 4) {
+    for (int64_t c0 = lane; c0 < cpr || first; c0 += 64 * 4) {
+      // every load is unconditional (clamped addresses); out-of-range data
+      // are zeroed only when used, so no load waits before all are issued
       u32x4 qv[kRB][4];
+      float wv[4][E];
 #pragma unroll
       for (int r = 0; r < kRB; ++r) {
         const int p = p0 + r;
-        const u32x4* yr = reinterpret_cast<const u32x4*>(Y + row_of(p < nrows ? p : p0) * ld);
+        const u32x4* yr = reinterpret_cast<const u32x4*>(Y + row_of(p < nrows ? p : 0) * ld);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int64_t c = c0 + 64 * u;
-          qv[r][u] = (p < nrows && c < cpr) ? yr[c] : u32x4{0u, 0u, 0u, 0u};
+          qv[r][u] = yr[c < cpr ? c : 0];
         }
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int64_t c = c0 + 64 * u;
-        if (c >= cpr) break;
-        const int64_t col0 = c * E;
-        float wv[E];
+        // whole 16-byte pieces of w where they exist, else clamped elements
+        const int64_t col0 = (c0 + 64 * u) * E;
         if (w_vec && col0 + E <= n) {
           const f32x4* w4 = reinterpret_cast<const f32x4*>(w + col0);
 #pragma unroll
           for (int h = 0; h < E / 4; ++h) {
             const f32x4 ww = w4[h];
-            wv[4 * h + 0] = ww.x;
-            wv[4 * h + 1] = ww.y;
-            wv[4 * h + 2] = ww.z;
-            wv[4 * h + 3] = ww.w;
+            wv[u][4 * h + 0] = ww.x;
+            wv[u][4 * h + 1] = ww.y;
+            wv[u][4 * h + 2] = ww.z;
+            wv[u][4 * h + 3] = ww.w;
           }
         } else {
 #pragma unroll
-          for (int e = 0; e < E; ++e) wv[e] = col0 + e < n ? w[col0 + e] : 0.f;
+          for (int e = 0; e < E; ++e) wv[u][e] = w[col0 + e < n ? col0 + e : n - 1];
         }
+      }
+      if (first) {
+        issued();
+        first = false;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = c0 + 64 * u;
 #pragma unroll
         for (int r = 0; r < kRB; ++r) {
           float f[E];
           Elems<T>::widen(qv[r][u], f);
+          const bool on = p0 + r < nrows && c < cpr;
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[r] = fmaf(f[e], wv[e], acc[r]);
+          for (int e = 0; e < E; ++e) {
+            const float ww = (on && c * E + e < n) ? wv[u][e] : 0.f;
+            acc[r] = fmaf(f[e], ww, acc[r]);
+          }
         }
       }
     }
@@ -128,6 +148,12 @@ __device__ __forceinline__ void margins(const T* Y, int64_t ld, int64_t n, const
       if (lane == 0 && p < nrows) out(p, row_of(p), tot);
     }
   }
+}
+
+template <typename T, typename RowOf, typename Out>
+__device__ __forceinline__ void margins(const T* Y, int64_t ld, int64_t n, const float* w, int nrows,
+                                        RowOf row_of, Out out, int wave, int lane) {
+  margins<T>(Y, ld, n, w, nrows, row_of, out, wave, lane, [] {});
 }
 
 // w[col] -= c * sum_rows Y[row][col] r[row] for the 16-byte column chunks

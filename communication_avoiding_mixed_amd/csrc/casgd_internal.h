@@ -82,7 +82,7 @@ struct ChainArgs {
   int* status;               // bit 0 set if an exchange wait expired
   int preload;               // set by launch_chain: own rows of G staged in LDS
 };
-size_t chain_lds_bytes(int s, int b, int Q);
+size_t chain_lds_bytes(int s, int b, int Q, int64_t ld);
 int chain_workgroups(int s, int b);
 constexpr int kChainMaxWorkgroups = 64;
 hipError_t launch_chain(int storage, int loss, const ChainArgs& a, hipStream_t stream,

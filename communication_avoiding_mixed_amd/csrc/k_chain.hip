@@ -19,6 +19,8 @@
 // bounded: on expiry the kernel flags an error in `status` and returns.
 // After the last inner step every workgroup holds all of r and updates its
 // own slice of columns of w in a fixed summation order (no float atomics).
+#include <type_traits>
+
 #include "casgd_chain.h"
 #include "casgd_gather.h"
 #include "casgd_gram.h"
@@ -55,11 +57,13 @@ __host__ __device__ inline int fast_cols(int64_t nown_max, int64_t cpl) {
   return (nown_max == 1 && cpl == 1) ? 1 : (nown_max <= 2 && cpl <= 2) ? 2 : kMaxCpl;
 }
 
+constexpr int64_t kWlMax = 2048;  // w staged in LDS for ld up to this
+
 struct ChainLayout {
-  int64_t rs, vown, yown, acc, acc_len, region, region_len, total;
+  int64_t rs, vown, yown, acc, acc_len, region, region_len, wl, wl_len, total;
 };
 
-__host__ __device__ inline ChainLayout chain_layout(int s, int b, int Q, bool preload) {
+__host__ __device__ inline ChainLayout chain_layout(int s, int b, int Q, int64_t ld, bool preload) {
   ChainLayout L;
   const int64_t sb = static_cast<int64_t>(s) * b;
   const int64_t nown_max = (b + Q - 1) / Q;
@@ -75,7 +79,9 @@ __host__ __device__ inline ChainLayout chain_layout(int s, int b, int Q, bool pr
   L.region = L.acc + L.acc_len;
   const int64_t gl = preload ? nown_max * b * (static_cast<int64_t>(s) * (s - 1) / 2) : 0;
   L.region_len = gl > 2048 ? gl : 2048;
-  L.total = L.region + L.region_len;
+  L.wl = L.region + L.region_len;
+  L.wl_len = ld <= kWlMax ? ld : 0;
+  L.total = L.wl + L.wl_len;
   return L;
 }
 
@@ -102,6 +108,48 @@ __device__ __forceinline__ void lds_publish(int* flag, int v) {
   __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// This workgroup's rows of every block-row of G, copied to LDS: own row t of
+// block-row j is a contiguous run of j*b/4 float4 in G and in LDS (at
+// t*P/4 + (b/4) j(j-1)/2).  Slots enumerate (t, j, c4) on power-of-two
+// strides so a slot decodes with shifts; slots past a run's end are skipped.
+struct GPreload {
+  const f32x4* G4;
+  f32x4* gl4;
+  int64_t T4, P4;  // slots (0: nothing to copy), float4 per own row
+  int lgW, lgJ, s, b, b4, q, Q;
+
+  __device__ __forceinline__ bool slot(int64_t g, int64_t& src, int64_t& dst) const {
+    const int c4 = static_cast<int>(g & ((1 << lgW) - 1));
+    const int j = 1 + static_cast<int>((g >> lgW) & ((1 << lgJ) - 1));
+    const int t = static_cast<int>(g >> (lgW + lgJ));
+    if (g >= T4 || j >= s || c4 >= j * b4) return false;
+    const int64_t tri = static_cast<int64_t>(j) * (j - 1) / 2;
+    const int64_t i = q + static_cast<int64_t>(Q) * t;
+    src = (static_cast<int64_t>(b) * b * tri + i * j * b) / 4 + c4;
+    dst = t * P4 + b4 * tri + c4;
+    return true;
+  }
+  // N slots g0, g0 + stride, ...: unconditional loads (skipped slots read
+  // G's first float4), then the stores of the slots that exist
+  template <int N>
+  __device__ __forceinline__ void issue(f32x4 (&tmp)[N], int64_t g0, int stride) const {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      int64_t src = 0, dst = 0;
+      slot(g0 + static_cast<int64_t>(stride) * u, src, dst);
+      tmp[u] = G4[src];
+    }
+  }
+  template <int N>
+  __device__ __forceinline__ void store(const f32x4 (&tmp)[N], int64_t g0, int stride) const {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      int64_t src = 0, dst = 0;
+      if (slot(g0 + static_cast<int64_t>(stride) * u, src, dst)) gl4[dst] = tmp[u];
+    }
+  }
+};
+
 // Everything a fast-path recurrence needs from chain_body.
 struct FastCtx {
   const ChainArgs* a;
@@ -112,16 +160,24 @@ struct FastCtx {
   const unsigned long long* mbox;
 };
 
+constexpr int kUpdRows = 4;  // rows per lane per block the update wave prefetches
+
 // Inner recurrence, fast path, for at most NO own rows per minibatch and CP
-// columns per lane (b <= 64 CP).  Wave 0 alone is on the critical
-// path: it collects r of block j-1 from its mailbox (lane l holds columns
-// l, l+64, ...), finishes z of its rows of block j with the one block
-// G_{j,j-1} on top of the per-lane partial sums, reduces once, and
-// publishes r.  Waves 1..3 fold each block t of r into the per-lane
-// partial sums of the rows of blocks k >= t+2 while wave 0 waits for the
-// next block, so z_j = v_j - c * sum_lanes(acc_j + G_{j,j-1} r_{j-1}).
-template <int LOSS, int NO, int CP>
-__device__ __forceinline__ void recurrence_fast(const FastCtx& x) {
+// columns per lane (b <= 64 CP).  Wave 0 alone is on the critical path: it
+// collects r of block j-1 from its mailbox (lane l holds columns l, l+64,
+// ...), finishes z of its rows of block j with the one block G_{j,j-1} on
+// top of the per-lane partial sums, reduces once, and publishes r.  The fold
+// waves fold each block t of r into the per-lane partial sums of the rows of
+// blocks k >= t+2 while wave 0 waits for the next block, so
+//   z_j = v_j - c * sum_lanes(acc_j + G_{j,j-1} r_{j-1}).
+// When the workgroup's column slice of w allows (at most 64 chunks, at most
+// kUpdRows rows per lane per block), wave 3 accumulates the update
+// Y^T r of its columns block by block as r arrives (the rows of the next
+// block prefetched), reduces over its lanes and writes w: then the waves
+// that fold are 1 and 2 and the function returns true.  Otherwise waves 1..3
+// fold and the caller runs the update afterwards.
+template <typename T, int LOSS, int NO, int CP>
+__device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
   const ChainArgs& a = *x.a;
   const int s = a.s, b = a.b, Q = a.Q, sb = s * b;
   const int q = x.q, nown = x.nown, nown_max = x.nown_max, lane = x.lane;
@@ -142,6 +198,16 @@ __device__ __forceinline__ void recurrence_fast(const FastCtx& x) {
   const int wave = x.wave;
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
   constexpr int LWc = 64 * CP;  // acc row pitch
+  // the update plan (same in every wave)
+  constexpr int E = Elems<T>::E;
+  const int64_t cpr = a.ld / E;
+  const int64_t per = (cpr + Q - 1) / Q;
+  int cw = 1;
+  while (cw < per && cw < 64) cw <<= 1;
+  const int rgw = 64 / cw;
+  const int rpl = (b + rgw - 1) / rgw;
+  const bool upd = per <= 64 && rpl <= kUpdRows;
+  const int nf = upd ? kWaves - 2 : kWaves - 1;  // fold waves
   if (wv == 0) {
     float rp[CP];
 #pragma unroll
@@ -152,7 +218,7 @@ __device__ __forceinline__ void recurrence_fast(const FastCtx& x) {
       // read before the wait: G_{j,j-1} of the own rows, their margins and
       // labels, and their partial sums if the helper has finished them
       float gv[NO][CP], av[NO][CP], vj[NO], yj[NO];
-      const int* ready = &acc_ready[j % (kWaves - 1)];
+      const int* ready = &acc_ready[j % nf];
       const bool acc_now = j < 2 || __hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= j - 1;
       if (acc_now) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 #pragma unroll
@@ -213,11 +279,12 @@ __device__ __forceinline__ void recurrence_fast(const FastCtx& x) {
     if (!abort_flag) {
       const int jb = (s - 1) * b;
       for (int l = lane; l < b; l += 64) rs[jb + l] = chain::take(&mbox[jb + l], a.epoch, a.status, &abort_flag, 0);
+      if (!abort_flag) lds_publish(&r_ready, s);
     }
-  } else {
-    // helper wv - 1 owns the rows of the blocks k = wv - 1 (mod 3); after r
-    // of block tb is in, it folds G_{k,tb} r_tb into their partial sums for
-    // every k >= tb + 2, two blocks at a time with all loads issued first
+  } else if (wv <= nf) {
+    // fold wave h = wv - 1 owns the rows of the blocks k = h (mod nf); after
+    // r of block tb is in, it folds G_{k,tb} r_tb into their partial sums
+    // for every k >= tb + 2, two blocks at a time with all loads issued first
     const int h = wv - 1;
     for (int tb = 0; tb + 2 < s; ++tb) {
       if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status)) break;
@@ -228,12 +295,12 @@ __device__ __forceinline__ void recurrence_fast(const FastCtx& x) {
         rr[u] = (l < b) ? rs[tb * b + l] : 0.f;
       }
       int k0 = tb + 2;
-      k0 += (h - k0 % (kWaves - 1) + (kWaves - 1)) % (kWaves - 1);  // first k >= tb+2 with k = h (mod 3)
-      for (int k = k0; k < s; k += 2 * (kWaves - 1)) {
+      k0 += (h - k0 % nf + nf) % nf;  // first k >= tb+2 with k = h (mod nf)
+      for (int k = k0; k < s; k += 2 * nf) {
         float gb[2][NO][CP], ab[2][NO][CP];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int kk = k + e * (kWaves - 1);
+          const int kk = k + e * nf;
 #pragma unroll
           for (int t = 0; t < NO; ++t)
 #pragma unroll
@@ -246,7 +313,7 @@ __device__ __forceinline__ void recurrence_fast(const FastCtx& x) {
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int kk = k + e * (kWaves - 1);
+          const int kk = k + e * nf;
 #pragma unroll
           for (int t = 0; t < NO; ++t)
 #pragma unroll
@@ -259,6 +326,165 @@ __device__ __forceinline__ void recurrence_fast(const FastCtx& x) {
       }
       lds_publish(&acc_ready[h], tb + 1);
     }
+  } else if (upd) {
+    // update wave: this workgroup's chunks [ch0, ch1) of w; lane = (rgl, cl)
+    // sums rows rgl, rgl + rgw, ... of every block for chunk ch0 + cl
+    const int64_t ch0 = static_cast<int64_t>(q) * per;
+    const int64_t ch1 = ch0 + per < cpr ? ch0 + per : cpr;
+    const int cl = lane % cw, rgl = lane / cw;
+    const int64_t ch = ch0 + cl;
+    const bool col_ok = ch < ch1;
+    const u32x4* Y4 = reinterpret_cast<const u32x4*>(a.Y);
+    float accw[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) accw[e] = 0.f;
+    // rows of block tb (clamped to the last block) for this lane, unconditional loads
+    auto load_blk = [&](int tb, u32x4 (&dst)[kUpdRows]) {
+      const int tbc = tb < s ? tb : s - 1;
+#pragma unroll
+      for (int i = 0; i < kUpdRows; ++i) {
+        const int rl = rgl + rgw * i;
+        const bool ok = i < rpl && rl < b && col_ok;
+        dst[i] = Y4[(ok ? static_cast<int64_t>(tbc) * b + rl : 0) * cpr + (ok ? ch : 0)];
+      }
+    };
+    auto use_blk = [&](int tb, const u32x4 (&src)[kUpdRows]) -> bool {
+      if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status)) return false;
+#pragma unroll
+      for (int i = 0; i < kUpdRows; ++i) {
+        const int rl = rgl + rgw * i;
+        if (i < rpl && rl < b && col_ok) {
+          const float rr = rs[tb * b + rl];
+          float f[E];
+          Elems<T>::widen(src[i], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) accw[e] = fmaf(f[e], rr, accw[e]);
+        }
+      }
+      return true;
+    };
+    u32x4 ya[kUpdRows], yb[kUpdRows];
+    load_blk(0, ya);
+    bool ok = true;
+    for (int tb = 0; tb < s; tb += 2) {
+      load_blk(tb + 1, yb);
+      ok = use_blk(tb, ya);
+      if (!ok || tb + 1 >= s) break;
+      load_blk(tb + 2, ya);
+      ok = use_blk(tb + 1, yb);
+      if (!ok) break;
+    }
+    if (ok) {
+      for (int off = cw; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < E; ++e) accw[e] += __shfl_xor(accw[e], off, 64);
+      if (rgl == 0 && col_ok) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int64_t col = ch * E + e;
+          if (col < a.n) a.w[col] = a.w[col] - a.c * accw[e];
+        }
+      }
+    }
+  }
+  return upd;
+}
+
+// Margins x . w of the nrows own rows with w staged in LDS.  Every global
+// load of the first batch is issued before any is waited for: w (clamped
+// element loads, for the staging copy), the rows of Y, then whatever
+// `issued()` adds; w goes to LDS (zero past n) behind a workgroup barrier and
+// the dot products read it from there.  kRB rows per wave per batch; lane 0
+// calls out(p, row, value).  Called by the whole workgroup.
+template <typename T, typename RowOf, typename Out, typename Issued>
+__device__ __forceinline__ void margins_wlds(const T* Y, int64_t ld, int64_t n, const float* w, int nrows,
+                                             RowOf row_of, Out out, float* wl, Issued issued) {
+  constexpr int E = Elems<T>::E;
+  constexpr int kRB = 4;
+  constexpr int kWv = static_cast<int>(kWlMax / kThreads);  // w elements per thread
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t cpr = ld / E;
+  float wtmp[kWv];
+#pragma unroll
+  for (int e = 0; e < kWv; ++e) {
+    const int64_t col = threadIdx.x + static_cast<int64_t>(kThreads) * e;
+    wtmp[e] = w[col < n ? col : n - 1];
+  }
+  // One batch: kRB rows of this wave, 4 chunks per lane from c0.  The first
+  // batch is separate code (FIRST), so no wait placed for the later batches
+  // can hold back the loads `issued()` adds to the first.
+  auto batch = [&](auto first_tag, int pass, int64_t c0, float (&acc)[kRB]) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    const int p0 = (pass * kWaves + wave) * kRB;
+    u32x4 qv[kRB][4];
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) {
+      const int p = p0 + r;
+      const u32x4* yr = reinterpret_cast<const u32x4*>(Y + row_of(p < nrows ? p : 0) * ld);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = c0 + 64 * u;
+        qv[r][u] = yr[c < cpr ? c : 0];
+      }
+    }
+    if constexpr (FIRST) {
+      issued();
+      // the copies of w are touched only now, so no load above is waited
+      // for before every one of them is in flight
+#pragma unroll
+      for (int e = 0; e < kWv; ++e) asm volatile("" : "+v"(wtmp[e]) : : "memory");
+#pragma unroll
+      for (int e = 0; e < kWv; ++e) {
+        const int64_t col = threadIdx.x + static_cast<int64_t>(kThreads) * e;
+        if (col < ld) wl[col] = col < n ? wtmp[e] : 0.f;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t c = c0 + 64 * u;
+      const f32x4* w4 = reinterpret_cast<const f32x4*>(wl + (c < cpr ? c : 0) * E);
+      float wv[E];
+#pragma unroll
+      for (int h = 0; h < E / 4; ++h) {
+        const f32x4 ww = w4[h];
+        wv[4 * h + 0] = ww.x;
+        wv[4 * h + 1] = ww.y;
+        wv[4 * h + 2] = ww.z;
+        wv[4 * h + 3] = ww.w;
+      }
+#pragma unroll
+      for (int r = 0; r < kRB; ++r) {
+        float f[E];
+        Elems<T>::widen(qv[r][u], f);
+        const bool on = p0 + r < nrows && c < cpr;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[r] = fmaf(f[e], on ? wv[e] : 0.f, acc[r]);
+      }
+    }
+  };
+  auto finish = [&](int pass, const float (&acc)[kRB]) {
+    const int p0 = (pass * kWaves + wave) * kRB;
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) {
+      const float tot = group_sum<64>(acc[r]);
+      const int p = p0 + r;
+      if (lane == 0 && p < nrows) out(p, row_of(p), tot);
+    }
+  };
+  const int passes = (nrows + kWaves * kRB - 1) / (kWaves * kRB);
+  for (int pass = 0; pass < passes; ++pass) {
+    float acc[kRB];
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) acc[r] = 0.f;
+    int64_t c0 = lane;
+    if (pass == 0) {
+      batch(std::integral_constant<bool, true>{}, 0, c0, acc);
+      c0 += 64 * 4;
+    }
+    for (; c0 < cpr; c0 += 64 * 4) batch(std::integral_constant<bool, false>{}, pass, c0, acc);
+    finish(pass, acc);
   }
 }
 
@@ -272,7 +498,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
   const int lane = threadIdx.x & 63;
   const int nown = (b - q + Q - 1) / Q;  // rows q, q+Q, ... below b
   const int nown_max = (b + Q - 1) / Q;
-  const ChainLayout L = chain_layout(s, b, Q, a.preload);
+  const ChainLayout L = chain_layout(s, b, Q, a.ld, a.preload);
   const bool fast = L.acc_len > 0;
   const int cpl = (b + 63) / 64;
   float* rs = sm + L.rs;      // r of all rows done so far
@@ -293,67 +519,57 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
   const T* Y = static_cast<const T*>(a.Y);
   const int64_t P = static_cast<int64_t>(b) * (static_cast<int64_t>(s) * (s - 1) / 2);
 
-  // ---- this workgroup's rows of every block-row of G go to LDS, 16 loads in
-  // flight per lane; the first batch is issued before the margins so both
-  // wait on memory together.  Own row t of block-row j is a contiguous run of
-  // j*b/4 float4 in G and in LDS (at t*P/4 + (b/4) j(j-1)/2).  Slots
-  // enumerate (t, j, c4) on power-of-two strides so a slot decodes with
-  // shifts; slots past a run's end are skipped.
-  const int64_t P4 = P / 4;
-  const int b4 = b / 4;
-  int lgW = 0, lgJ = 0;
-  while ((1 << lgW) < (s - 1) * b4) ++lgW;
-  while ((1 << lgJ) < s - 1) ++lgJ;
-  const int64_t T4 = (a.preload && s > 1) ? static_cast<int64_t>(nown) << (lgW + lgJ) : 0;
-  const f32x4* G4 = reinterpret_cast<const f32x4*>(a.G);
-  f32x4* gl4 = reinterpret_cast<f32x4*>(gl);
-  auto slot = [&](int64_t g, int64_t& src, int64_t& dst) -> bool {
-    const int c4 = static_cast<int>(g & ((1 << lgW) - 1));
-    const int j = 1 + static_cast<int>((g >> lgW) & ((1 << lgJ) - 1));
-    const int t = static_cast<int>(g >> (lgW + lgJ));
-    if (g >= T4 || j >= s || c4 >= j * b4) return false;
-    const int64_t tri = static_cast<int64_t>(j) * (j - 1) / 2;
-    const int64_t i = q + static_cast<int64_t>(Q) * t;
-    src = (static_cast<int64_t>(b) * b * tri + i * j * b) / 4 + c4;
-    dst = t * P4 + b4 * tri + c4;
-    return true;
-  };
-  auto g_issue = [&](f32x4 (&tmp)[16], int64_t g0) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      int64_t src = 0, dst = 0;
-      slot(g0 + static_cast<int64_t>(kThreads) * u, src, dst);
-      tmp[u] = G4[src];  // skipped slots read G's first float4
-    }
-  };
-  auto g_store = [&](const f32x4 (&tmp)[16], int64_t g0) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      int64_t src = 0, dst = 0;
-      if (slot(g0 + static_cast<int64_t>(kThreads) * u, src, dst)) gl4[dst] = tmp[u];
-    }
-  };
+  // ---- this workgroup's rows of G to LDS (when a.preload), the first batch
+  // in flight beside the margins' loads.
+  GPreload gp;
+  gp.G4 = reinterpret_cast<const f32x4*>(a.G);
+  gp.gl4 = reinterpret_cast<f32x4*>(gl);
+  gp.P4 = P / 4;
+  gp.s = s;
+  gp.b = b;
+  gp.b4 = b / 4;
+  gp.q = q;
+  gp.Q = Q;
+  gp.lgW = 0;
+  gp.lgJ = 0;
+  while ((1 << gp.lgW) < (s - 1) * gp.b4) ++gp.lgW;
+  while ((1 << gp.lgJ) < s - 1) ++gp.lgJ;
+  gp.T4 = (a.preload && s > 1) ? static_cast<int64_t>(nown) << (gp.lgW + gp.lgJ) : 0;
+  const int64_t T4 = gp.T4;
+  constexpr int kGB = 8;  // float4 per lane per preload batch
   {
-    f32x4 tmp[16];
-    if (T4 > 0) g_issue(tmp, threadIdx.x);
-    // ---- margins of the own rows (row p = (j, t) is minibatch j's row q + Q t)
-    chain::margins<T>(
-        Y, a.ld, a.n, a.w, s * nown,
-        [&](int p) {
-          const int j = p / nown;
-          return static_cast<int64_t>(j) * b + q + static_cast<int64_t>(Q) * (p - j * nown);
-        },
-        [&](int p, int64_t row, float v) {
-          const int j = p / nown;
-          vown[j * nown_max + (p - j * nown)] = v;
-          yown[j * nown_max + (p - j * nown)] = a.yB[row];
-          a.v[row] = v;
-        },
-        wave, lane);
-    if (T4 > 0) g_store(tmp, threadIdx.x);
-    for (int64_t f0 = threadIdx.x + kThreads * 16; f0 < T4; f0 += kThreads * 16) {
-      g_issue(tmp, f0);
-      g_store(tmp, f0);
+    // own row p = (j, t) is minibatch j's row q + Q t; its label is loaded
+    // now and stored after the margins, so the load overlaps them
+    const int nrows = s * nown;
+    auto row_of = [&](int p) {
+      const int j = p / nown;
+      return static_cast<int64_t>(j) * b + q + static_cast<int64_t>(Q) * (p - j * nown);
+    };
+    auto slot_of = [&](int p) {
+      const int j = p / nown;
+      return j * nown_max + (p - j * nown);
+    };
+    // (an unconditional load: a load under a branch is waited for at the join)
+    const int yp = static_cast<int>(threadIdx.x) < nrows ? static_cast<int>(threadIdx.x) : nrows - 1;
+    const float ylab = a.yB[row_of(yp)];
+    f32x4 tmp[kGB];
+    auto out = [&](int p, int64_t row, float v) {
+      vown[slot_of(p)] = v;
+      a.v[row] = v;
+    };
+    auto more = [&] {
+      if (T4 > 0) gp.issue<kGB>(tmp, threadIdx.x, kThreads);
+    };
+    if (L.wl_len > 0)
+      margins_wlds<T>(Y, a.ld, a.n, a.w, nrows, row_of, out, sm + L.wl, more);
+    else
+      chain::margins<T>(Y, a.ld, a.n, a.w, nrows, row_of, out, wave, lane, more);
+    if (static_cast<int>(threadIdx.x) < nrows) yown[slot_of(threadIdx.x)] = ylab;
+    for (int p = threadIdx.x + kThreads; p < nrows; p += kThreads) yown[slot_of(p)] = a.yB[row_of(p)];
+    if (T4 > 0) gp.store<kGB>(tmp, threadIdx.x, kThreads);
+    for (int64_t g0 = threadIdx.x + kThreads * kGB; g0 < T4; g0 += kThreads * kGB) {
+      gp.issue<kGB>(tmp, g0, kThreads);
+      gp.store<kGB>(tmp, g0, kThreads);
     }
   }
   __syncthreads();  // vown, acc, flags and the G rows ready
@@ -364,11 +580,12 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
   if (fast) {
     FastCtx x{&a, q, nown, nown_max, lane, wave, rs, vown, yown, acc, gl, P, &abort_flag, &r_ready, acc_ready, mbox};
     const int fc = fast_cols(nown_max, cpl);
-    if (fc == 1) recurrence_fast<LOSS, 1, 1>(x);
-    else if (fc == 2) recurrence_fast<LOSS, 2, 2>(x);
-    else recurrence_fast<LOSS, kMaxOwn, kMaxCpl>(x);
+    bool updated;
+    if (fc == 1) updated = recurrence_fast<T, LOSS, 1, 1>(x);
+    else if (fc == 2) updated = recurrence_fast<T, LOSS, 2, 2>(x);
+    else updated = recurrence_fast<T, LOSS, kMaxOwn, kMaxCpl>(x);
     __syncthreads();
-    if (abort_flag) return;
+    if (abort_flag || updated) return;
   } else {
     // ---- inner recurrence, any b.  Waves 1..3 compute and publish the own rows;
     // wave 0 only polls for the step's r values, so its waits never queue
@@ -544,13 +761,13 @@ hipError_t chain_t(const ChainArgs& a, size_t lds, hipStream_t st, const LaunchT
 
 }  // namespace
 
-bool chain_preload(int s, int b, int Q) {
+bool chain_preload(int s, int b, int Q, int64_t ld) {
   if ((b & 3) != 0) return false;
-  return static_cast<size_t>(chain_layout(s, b, Q, true).total) * sizeof(float) <= kLdsBudget;
+  return static_cast<size_t>(chain_layout(s, b, Q, ld, true).total) * sizeof(float) <= kLdsBudget;
 }
 
-size_t chain_lds_bytes(int s, int b, int Q) {
-  const size_t need = static_cast<size_t>(chain_layout(s, b, Q, chain_preload(s, b, Q)).total) * sizeof(float);
+size_t chain_lds_bytes(int s, int b, int Q, int64_t ld) {
+  const size_t need = static_cast<size_t>(chain_layout(s, b, Q, ld, chain_preload(s, b, Q, ld)).total) * sizeof(float);
   return need > kLdsReserve ? need : kLdsReserve;
 }
 
@@ -562,8 +779,8 @@ int chain_workgroups(int s, int b) {
 hipError_t launch_chain(int storage, int loss, const ChainArgs& a_in, hipStream_t st,
                         const LaunchTimer& tm) {
   ChainArgs a = a_in;
-  a.preload = chain_preload(a.s, a.b, a.Q) ? 1 : 0;
-  const size_t lds = chain_lds_bytes(a.s, a.b, a.Q);
+  a.preload = chain_preload(a.s, a.b, a.Q, a.ld) ? 1 : 0;
+  const size_t lds = chain_lds_bytes(a.s, a.b, a.Q, a.ld);
   if (storage == kStoreBF16) {
     if (loss == kLogistic) return chain_t<uint16_t, kLogistic>(a, lds, st, tm);
     if (loss == kSquared) return chain_t<uint16_t, kSquared>(a, lds, st, tm);
@@ -576,8 +793,8 @@ hipError_t launch_chain(int storage, int loss, const ChainArgs& a_in, hipStream_
 
 hipError_t launch_pipe(int loss, const PipeArgs& p_in, hipStream_t st, const LaunchTimer& tm) {
   PipeArgs p = p_in;
-  p.a.preload = chain_preload(p.a.s, p.a.b, p.a.Q) ? 1 : 0;
-  size_t lds = chain_lds_bytes(p.a.s, p.a.b, p.a.Q);
+  p.a.preload = chain_preload(p.a.s, p.a.b, p.a.Q, p.a.ld) ? 1 : 0;
+  size_t lds = chain_lds_bytes(p.a.s, p.a.b, p.a.Q, p.a.ld);
   const size_t glds = sizeof(uint16_t) * (gram_variant(p.a.ld) == 0 ? gram::lds_elems<32>() : gram::lds_elems<64>());
   if (glds > lds) lds = glds;
   const int grid = p.gath_wgs > 0 ? p.gath0 + p.gath_wgs : (p.gram_slots > 0 ? p.gram0 + p.gram_slots : p.a.Q);

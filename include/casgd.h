@@ -189,12 +189,15 @@ enum casgd_option {
  * unknown option or value. */
 int casgd_set_option(casgd_handle h, int option, int value);
 
-/* Time every hot-path kernel launch (on != 0) with HIP events that the
- * kernel's own dispatch stamps at its start and end. */
+/* Time hot-path kernel launches with HIP events that the kernel's own
+ * dispatch stamps at its start and end.  on = 0: off; on = 1: every launch;
+ * on = k > 1: every k-th launch of each kernel (the first one included), so
+ * the stamping perturbs a long run less.  EINVAL for on < 0. */
 int casgd_set_timing(casgd_handle h, int on);
 
-/* Total milliseconds and launch count of one kernel (enum casgd_kernel_id)
- * since timing was switched on; synchronises.  reset != 0 clears it after. */
+/* Total milliseconds and count of the timed launches of one kernel (enum
+ * casgd_kernel_id) since timing was switched on; synchronises.  reset != 0
+ * clears them after. */
 int casgd_get_timing(casgd_handle h, int kernel, double* total_ms, int64_t* launches,
                      int reset);
 

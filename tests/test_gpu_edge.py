@@ -75,6 +75,8 @@ def test_ragged_and_degenerate_shapes(loss, m, n, s, b):
     (5000, 64, 20, 64),   # helpers own 2 rows each (LDS), far sums over 16 steps
     (4000, 72, 30, 48),   # helpers own 1 row each
     (3000, 50, 9, 64),    # b at the lookahead limit, ld 64
+    (3000, 1800, 3, 128),  # 8 rows per lane per block: update after the recurrence
+    (1500, 3000, 2, 32),   # ld 3008: weights read from global memory in the margins
 ])
 def test_lookahead_and_all_to_all_recurrences(loss, m, n, s, b, rec):
     X = synth.make_uniform((m, n), seed=m + s, lo=-0.4, hi=0.4)

@@ -38,6 +38,8 @@ def _data(loss, m, n, seed):
     (900, 40, 6, 16, 1),      # prologue only, then one launch
     (900, 40, 6, 16, 2),      # no gather role in either launch
     (4000, 2000, 16, 64, 3),  # the epsilon step shape
+    (3000, 1800, 3, 128, 3),  # update after the recurrence (8 rows per lane per block)
+    (2000, 3000, 2, 32, 3),   # ld 3008: weights read from global memory in the margins
 ])
 def test_train_equals_outer_steps(loss, m, n, s, b, n_outer):
     import torch
@@ -108,3 +110,19 @@ def test_pipe_timer_counts_launches():
     h.set_timing(False)
     assert cnt == 7 and ms > 0
     assert g_cnt == 2  # prologue: steps 0 and 1
+
+
+def test_sampled_timing_stamps_every_kth_launch():
+    import torch
+    name = "logistic-4096x64"
+    wl = synth.WORKLOADS[name]
+    X, y = synth.make_data(name)
+    h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss)
+    w = torch.zeros(wl.n, device="cuda")
+    h.set_timing(True, every=3)
+    h.train(wl.s, wl.b, wl.eta, 0, 0, 10, w)
+    ms, cnt = h.timing(B.K_PIPE, reset=True)
+    h.set_timing(False)
+    assert cnt == 4 and ms > 0  # launches 0, 3, 6, 9
+    with pytest.raises(B.CasgdError):
+        h.set_timing(True, every=-1)
