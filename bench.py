@@ -113,6 +113,40 @@ def cpu_baseline(X, y, wl, budget_s: float):
     }
 
 
+def sgd_baselines(h_bf16, X, y, wl, steps: int, warmup: int, dev):
+    """Plain minibatch SGD with the same library: s = 1 outer steps (margins
+    and update of one minibatch, no Gram), b and eta as the workload, the
+    same number of inner steps as the timed CA-SGD run.  float32 storage is
+    the baseline the method is compared with; bf16 storage separates the
+    effect of the s-step formulation from that of the storage type."""
+    import torch
+    from communication_avoiding_mixed_amd import binding as B
+    n_inner = wl.s * steps
+    out = {}
+    stream = torch.cuda.Stream()
+    for storage in ("fp32", "bf16"):
+        h = h_bf16 if storage == "bf16" else B.CASGD(torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev),
+                                                     wl.loss, "fp32")
+        w = torch.zeros(wl.n, device=dev)
+        with torch.cuda.stream(stream):
+            h.train(1, wl.b, wl.eta, 7, 0, warmup * wl.s, w)
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record(stream)
+            h.train(1, wl.b, wl.eta, 7, warmup * wl.s, n_inner, w)
+            stop.record(stream)
+            torch.cuda.synchronize()
+        ms = start.elapsed_time(stop)
+        out[storage] = {"value": n_inner / (ms / 1e3), "unit": "inner SGD steps/s", "steps": n_inner,
+                        "us_per_step": ms * 1e3 / n_inner}
+        if h is not h_bf16:
+            h.close()
+            del h
+            torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(nbytes: int):
     """One plain device copy of nbytes (reads nbytes, writes nbytes), timed."""
     import torch
@@ -135,6 +169,8 @@ def main():
     ap.add_argument("--workload", default="epsilon")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sgd-baseline", action="store_true",
+                    help="skip the plain minibatch SGD runs (s = 1) of the same library")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES between two device buffers (a plain copy kernel of "
                          "known traffic, to scale the HBM byte counters) and exit")
@@ -207,6 +243,7 @@ def main():
         h.set_timing(False)
     ms_per_step = ms / args.steps
     value = wl.s * args.steps / (ms / 1e3)
+    sgd = None if args.no_sgd_baseline else sgd_baselines(h, X, y, wl, args.steps, args.warmup, dev)
 
     alg = algorithmic(wl)
     gram_tflops = alg["gram_flops"] / (per["gram"] * 1e-6) / 1e12
@@ -260,6 +297,10 @@ def main():
         "kernels": kernels,
         "final_loss": loss,
     }
+    if sgd:
+        out["sgd_baseline"] = {"kind": "minibatch SGD, s = 1, same library and b, eta", **sgd}
+        out["speedup_vs_fp32_sgd"] = value / sgd["fp32"]["value"]
+        out["speedup_vs_bf16_sgd"] = value / sgd["bf16"]["value"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(X, y, wl, args.cpu_budget)
     print(json.dumps(out), flush=True)

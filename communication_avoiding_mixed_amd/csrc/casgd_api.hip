@@ -297,7 +297,7 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   return CASGD_OK;
 }
 
-// casgd_train's pipelined loop (bf16 storage, all-to-all recurrence): step i
+// casgd_train's pipelined loop (all-to-all recurrence): step i
 // uses buffer set i mod 3.  Prologue: gather and Gram of step 0, gather of
 // step 1.  Launch i: chain of step i, Gram of step i+1, gather of step i+2.
 // The gather of step i+2 overwrites the set of step i-1, whose chain ended
@@ -336,7 +336,7 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
   if (e != hipSuccess) return hip_fail(e, "pipeline prologue");
 
   const int Q = casgd::chain_workgroups(s, b);
-  const int64_t cpr = h->ld / 8;
+  const int64_t cpr = h->ld / (h->storage == CASGD_BF16 ? 8 : 4);  // 16-byte chunks per row
   const int gs = casgd::gather::group_size(cpr);
   const int rows_per_wg = 256 / gs;
   const int gather_wgs_all = (sb + rows_per_wg - 1) / rows_per_wg;
@@ -366,7 +366,7 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
       const StepBuffers& N = h->buf[(i + 1) % 3];
       p.gram_slots = plan.slots;
       p.tps = (b + 63) / 64;
-      p.gY = static_cast<const uint16_t*>(N.Y);
+      p.gY = N.Y;
       p.gG = N.G;
       p.order = h->order;
     }
@@ -386,7 +386,7 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
       p.yBo = A.yB;
     }
     e = timed(h, CASGD_K_PIPE, [&](const casgd::LaunchTimer& tm) {
-      return casgd::launch_pipe(h->loss, p, h->stream, tm);
+      return casgd::launch_pipe(h->storage, h->loss, p, h->stream, tm);
     });
     if (e != hipSuccess) return hip_fail(e, "pipelined step launch");
   }
@@ -546,7 +546,7 @@ int casgd_train(casgd_handle h, int s, int b, float eta, uint64_t base_seed, uin
   int rc = check_step_args(h, s, b, w);
   if (rc != CASGD_OK) return rc;
   if (n_outer < 0) return fail(CASGD_EINVAL, "n_outer must be >= 0");
-  if (n_outer > 0 && h->storage == CASGD_BF16 && h->recurrence != 2)
+  if (n_outer > 0 && h->recurrence != 2)
     return run_train_pipe(h, s, b, eta, base_seed, first_step, n_outer, w);
   for (int k = 0; k < n_outer; ++k) {
     rc = run_outer(h, s, b, eta, casgd::splitmix64(base_seed, first_step + k), nullptr, w);

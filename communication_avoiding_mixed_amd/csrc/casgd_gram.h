@@ -1,7 +1,8 @@
-// One 64 x 64 output tile of the strictly-lower block triangle of G = Y Y^T
-// on bf16 MFMA (v_mfma_f32_32x32x16_bf16, float32 accumulators), as a device
-// function so both the stand-alone Gram kernel and the pipelined step kernel
-// run the same code.  The Abstract of "Mixed-Precision Communication-Avoiding
+// One 64 x 64 output tile of the strictly-lower block triangle of G = Y Y^T,
+// on bf16 MFMA (v_mfma_f32_32x32x16_bf16, float32 accumulators) for bf16
+// storage or on the vector ALUs for float32 storage, as device functions so
+// both the stand-alone Gram kernel and the pipelined step kernel run the same
+// code.  The Abstract of "Mixed-Precision Communication-Avoiding
 // SGD for Generalized Linear Models on GPUs" forms the Gram from low-precision
 // inputs with high-precision accumulation on the matrix hardware.
 //
@@ -146,6 +147,76 @@ __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ Y, int64_
     for (int e = 0; e < 16; ++e) {
       const int row = a0 + wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
       if (row < b) gcol[row * ldg] = acc[0][e];
+    }
+  }
+}
+
+// float32 storage: the same tiles on the vector ALUs, each lane a 4 x 4
+// register block, K in 16-wide stages through LDS.  `lds` holds
+// kF32LdsElems floats.
+constexpr int kF32BK = 16;
+constexpr int kF32LdsElems = 2 * kF32BK * (kTile + 4);
+
+__device__ __forceinline__ void f32_tile(const float* __restrict__ Y, int64_t ld, int b, int tps,
+                                         float* __restrict__ G, int tile, float* lds) {
+  constexpr int BK = kF32BK;
+  constexpr int LW = kTile + 4;
+  float* As = lds;            // [BK][LW]
+  float* Bs = lds + BK * LW;  // [BK][LW]
+  const int nt2 = tps * tps;
+  const int p = tile / nt2;
+  const int rem = tile - p * nt2;
+  const int ti = rem / tps;
+  const int tj = rem - ti * tps;
+  int j, t;
+  block_of(p, j, t);
+  float* Gj = G + static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
+  const int64_t ldg = static_cast<int64_t>(j) * b;
+  const int a0 = ti * kTile, b0 = tj * kTile;
+
+  // loader: 64 rows x 16 k per stage = 256 float4
+  const int lr = threadIdx.x >> 2;
+  const int lk = (threadIdx.x & 3) * 4;
+  const bool aok = a0 + lr < b, bok = b0 + lr < b;
+  const float* ap = Y + (static_cast<int64_t>(j) * b + a0 + (aok ? lr : 0)) * ld + lk;
+  const float* bp = Y + (static_cast<int64_t>(t) * b + b0 + (bok ? lr : 0)) * ld + lk;
+
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4] = {};
+  for (int64_t k0 = 0; k0 < ld; k0 += BK) {
+    const bool kin = k0 + lk < ld;
+    const float4 av = (aok && kin) ? *reinterpret_cast<const float4*>(ap + k0) : make_float4(0, 0, 0, 0);
+    const float4 bv = (bok && kin) ? *reinterpret_cast<const float4*>(bp + k0) : make_float4(0, 0, 0, 0);
+    As[(lk + 0) * LW + lr] = av.x;
+    As[(lk + 1) * LW + lr] = av.y;
+    As[(lk + 2) * LW + lr] = av.z;
+    As[(lk + 3) * LW + lr] = av.w;
+    Bs[(lk + 0) * LW + lr] = bv.x;
+    Bs[(lk + 1) * LW + lr] = bv.y;
+    Bs[(lk + 2) * LW + lr] = bv.z;
+    Bs[(lk + 3) * LW + lr] = bv.w;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < BK; ++k) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&As[k * LW + ty * 4]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&Bs[k * LW + tx * 4]);
+      const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[u][q] = fmaf(a[u], bb[q], acc[u][q]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = a0 + ty * 4 + u;
+    if (row >= b) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = b0 + tx * 4 + q;
+      if (col < b) Gj[row * ldg + static_cast<int64_t>(t) * b + col] = acc[u][q];
     }
   }
 }

@@ -88,7 +88,7 @@ constexpr int kChainMaxWorkgroups = 64;
 hipError_t launch_chain(int storage, int loss, const ChainArgs& a, hipStream_t stream,
                         const LaunchTimer& tm = {});
 
-// One launch of the pipelined training loop (bf16 storage): the chain of
+// One launch of the pipelined training loop: the chain of
 // outer step k on workgroups [0, a.Q), the Gram of step k+1 (gram_slots > 0)
 // on [gram0, gram0 + gram_slots) with gram0 a multiple of kXcds, and the
 // sample + gather of step k+2 (gath_wgs > 0) on [gath0, gath0 + gath_wgs).
@@ -97,7 +97,7 @@ hipError_t launch_chain(int storage, int loss, const ChainArgs& a, hipStream_t s
 struct PipeArgs {
   ChainArgs a;
   int gram0 = 0, gram_slots = 0, tps = 0;
-  const uint16_t* gY = nullptr;  // Y of step k+1
+  const void* gY = nullptr;  // Y of step k+1 (stored type)
   float* gG = nullptr;           // G of step k+1
   const int* order = nullptr;
   int gath0 = 0, gath_wgs = 0, gs = 0;  // gs: lanes per row (gather::group_size)
@@ -110,7 +110,8 @@ struct PipeArgs {
   void* Yo = nullptr;
   float* yBo = nullptr;
 };
-hipError_t launch_pipe(int loss, const PipeArgs& p, hipStream_t stream, const LaunchTimer& tm = {});
+hipError_t launch_pipe(int storage, int loss, const PipeArgs& p, hipStream_t stream,
+                       const LaunchTimer& tm = {});
 
 // Lookahead form of the same kernel (one critical workgroup for the d latest
 // blocks of every step, M helpers for the rest, receivers for the update);

@@ -696,18 +696,25 @@ __device__ __forceinline__ void pipe_gather(const PipeArgs& p, int g) {
                          row0 + static_cast<int>(threadIdx.x) / GS, threadIdx.x % GS);
 }
 
-template <int LOSS, int BK, int D>
+// T = uint16_t: bf16 storage, Gram on MFMA with (BK, D) stages; T = float:
+// float32 storage, Gram on the vector ALUs (BK, D unused).
+template <typename T, int LOSS, int BK, int D>
 __global__ __launch_bounds__(kThreads) void pipe_kernel(PipeArgs p) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   const int w = blockIdx.x;
   if (w < p.a.Q) {
-    chain_body<uint16_t, LOSS>(p.a, w);
+    chain_body<T, LOSS>(p.a, w);
     return;
   }
   if (w >= p.gram0 && w < p.gram0 + p.gram_slots) {
     const int tile = p.order[w - p.gram0];
-    if (tile >= 0)
-      gram::bf16_tile<BK, D>(p.gY, p.a.ld, p.a.b, p.tps, p.gG, tile, reinterpret_cast<uint16_t*>(sm));
+    if (tile >= 0) {
+      if constexpr (std::is_same<T, float>::value)
+        gram::f32_tile(static_cast<const float*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile, sm);
+      else
+        gram::bf16_tile<BK, D>(static_cast<const uint16_t*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile,
+                               reinterpret_cast<uint16_t*>(sm));
+    }
     return;
   }
   if (w >= p.gath0 && w < p.gath0 + p.gath_wgs) {
@@ -722,26 +729,27 @@ __global__ __launch_bounds__(kThreads) void pipe_kernel(PipeArgs p) {
   }
 }
 
-template <int LOSS, int BK, int D>
+template <typename T, int LOSS, int BK, int D>
 hipError_t pipe_t(const PipeArgs& p, int grid, size_t lds, hipStream_t st, const LaunchTimer& tm) {
   static size_t granted = 64 * 1024;
   if (lds > granted) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pipe_kernel<LOSS, BK, D>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pipe_kernel<T, LOSS, BK, D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
     granted = lds;
   }
-  return launch_kernel(pipe_kernel<LOSS, BK, D>, dim3(grid), dim3(kThreads), lds, st, tm, p);
+  return launch_kernel(pipe_kernel<T, LOSS, BK, D>, dim3(grid), dim3(kThreads), lds, st, tm, p);
 }
 
 template <int LOSS>
-hipError_t pipe_l(const PipeArgs& p, int grid, size_t lds, hipStream_t st, const LaunchTimer& tm) {
+hipError_t pipe_l(int storage, const PipeArgs& p, int grid, size_t lds, hipStream_t st, const LaunchTimer& tm) {
+  if (storage != kStoreBF16) return pipe_t<float, LOSS, 0, 0>(p, grid, lds, st, tm);
   switch (gram_variant(p.a.ld)) {
-    case 0: return pipe_t<LOSS, 32, 1>(p, grid, lds, st, tm);
-    case 1: return pipe_t<LOSS, 64, 8>(p, grid, lds, st, tm);
-    case 2: return pipe_t<LOSS, 64, 4>(p, grid, lds, st, tm);
-    default: return pipe_t<LOSS, 64, 2>(p, grid, lds, st, tm);
+    case 0: return pipe_t<uint16_t, LOSS, 32, 1>(p, grid, lds, st, tm);
+    case 1: return pipe_t<uint16_t, LOSS, 64, 8>(p, grid, lds, st, tm);
+    case 2: return pipe_t<uint16_t, LOSS, 64, 4>(p, grid, lds, st, tm);
+    default: return pipe_t<uint16_t, LOSS, 64, 2>(p, grid, lds, st, tm);
   }
 }
 
@@ -791,16 +799,17 @@ hipError_t launch_chain(int storage, int loss, const ChainArgs& a_in, hipStream_
   return chain_t<float, kPoisson>(a, lds, st, tm);
 }
 
-hipError_t launch_pipe(int loss, const PipeArgs& p_in, hipStream_t st, const LaunchTimer& tm) {
+hipError_t launch_pipe(int storage, int loss, const PipeArgs& p_in, hipStream_t st, const LaunchTimer& tm) {
   PipeArgs p = p_in;
   p.a.preload = chain_preload(p.a.s, p.a.b, p.a.Q, p.a.ld) ? 1 : 0;
   size_t lds = chain_lds_bytes(p.a.s, p.a.b, p.a.Q, p.a.ld);
-  const size_t glds = sizeof(uint16_t) * (gram_variant(p.a.ld) == 0 ? gram::lds_elems<32>() : gram::lds_elems<64>());
+  const size_t glds = storage != kStoreBF16 ? sizeof(float) * gram::kF32LdsElems
+                      : sizeof(uint16_t) * (gram_variant(p.a.ld) == 0 ? gram::lds_elems<32>() : gram::lds_elems<64>());
   if (glds > lds) lds = glds;
   const int grid = p.gath_wgs > 0 ? p.gath0 + p.gath_wgs : (p.gram_slots > 0 ? p.gram0 + p.gram_slots : p.a.Q);
-  if (loss == kLogistic) return pipe_l<kLogistic>(p, grid, lds, st, tm);
-  if (loss == kSquared) return pipe_l<kSquared>(p, grid, lds, st, tm);
-  return pipe_l<kPoisson>(p, grid, lds, st, tm);
+  if (loss == kLogistic) return pipe_l<kLogistic>(storage, p, grid, lds, st, tm);
+  if (loss == kSquared) return pipe_l<kSquared>(storage, p, grid, lds, st, tm);
+  return pipe_l<kPoisson>(storage, p, grid, lds, st, tm);
 }
 
 }  // namespace casgd

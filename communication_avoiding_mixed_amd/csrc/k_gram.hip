@@ -28,73 +28,14 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restri
   gram::bf16_tile<BK, D>(Y, ld, b, tps, G, tile, lds);
 }
 
-// float32 storage: the same tiles on the vector ALUs (each lane a 4 x 4
-// register block), used when the data are kept in float32.
+// float32 storage: the same tiles on the vector ALUs (casgd_gram.h).
 __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__ Y, int64_t ld,
                                                        int b, int tps, float* __restrict__ G,
                                                        const int* __restrict__ order) {
-  constexpr int BK = 16;
-  __shared__ float As[BK][kTile + 4];
-  __shared__ float Bs[BK][kTile + 4];
-  const int nt2 = tps * tps;
+  __shared__ __attribute__((aligned(16))) float lds[gram::kF32LdsElems];
   const int tile = order[blockIdx.x];
   if (tile < 0) return;
-  const int p = tile / nt2;
-  const int rem = tile - p * nt2;
-  const int ti = rem / tps;
-  const int tj = rem - ti * tps;
-  int j, t;
-  block_of(p, j, t);
-  const float* Yp = Y;
-  float* Gj = G + static_cast<int64_t>(b) * b * (static_cast<int64_t>(j) * (j - 1) / 2);
-  const int64_t ldg = static_cast<int64_t>(j) * b;
-  const int a0 = ti * kTile, b0 = tj * kTile;
-
-  // loader: 64 rows x 16 k per stage = 256 float4
-  const int lr = threadIdx.x >> 2;
-  const int lk = (threadIdx.x & 3) * 4;
-  const bool aok = a0 + lr < b, bok = b0 + lr < b;
-  const float* ap = Yp + (static_cast<int64_t>(j) * b + a0 + (aok ? lr : 0)) * ld + lk;
-  const float* bp = Yp + (static_cast<int64_t>(t) * b + b0 + (bok ? lr : 0)) * ld + lk;
-
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4] = {};
-  for (int64_t k0 = 0; k0 < ld; k0 += BK) {
-    const bool kin = k0 + lk < ld;
-    const float4 av = (aok && kin) ? *reinterpret_cast<const float4*>(ap + k0) : make_float4(0, 0, 0, 0);
-    const float4 bv = (bok && kin) ? *reinterpret_cast<const float4*>(bp + k0) : make_float4(0, 0, 0, 0);
-    As[lk + 0][lr] = av.x;
-    As[lk + 1][lr] = av.y;
-    As[lk + 2][lr] = av.z;
-    As[lk + 3][lr] = av.w;
-    Bs[lk + 0][lr] = bv.x;
-    Bs[lk + 1][lr] = bv.y;
-    Bs[lk + 2][lr] = bv.z;
-    Bs[lk + 3][lr] = bv.w;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < BK; ++k) {
-      const float4 a4 = *reinterpret_cast<const float4*>(&As[k][ty * 4]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&Bs[k][tx * 4]);
-      const float a[4] = {a4.x, a4.y, a4.z, a4.w};
-      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[u][q] = fmaf(a[u], bb[q], acc[u][q]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = a0 + ty * 4 + u;
-    if (row >= b) continue;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int col = b0 + tx * 4 + q;
-      if (col < b) Gj[row * ldg + static_cast<int64_t>(t) * b + col] = acc[u][q];
-    }
-  }
+  gram::f32_tile(Y, ld, b, tps, G, tile, lds);
 }
 
 }  // namespace

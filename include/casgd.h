@@ -126,7 +126,7 @@ int casgd_outer_step_indices(casgd_handle h, int s, int b, float eta,
  * n_outer consecutive outer iterations; outer step k (k = first_step ...
  * first_step + n_outer - 1) samples with seed casgd_step_seed(base_seed, k).
  * Bit-identical to calling casgd_outer_step with those seeds.  Asynchronous.
- * With bf16 storage and the default recurrence the loop is pipelined on the
+ * With the default recurrence the loop is pipelined on the
  * handle's stream alone: after a prologue (gather and Gram of the first step,
  * gather of the second), each step is ONE launch that runs the margins,
  * recurrence and update of step k next to the Gram of step k+1 and the

@@ -59,6 +59,23 @@ def test_train_equals_outer_steps(loss, m, n, s, b, n_outer):
         assert np.array_equal(got[k], h.export(k)), k
 
 
+@pytest.mark.parametrize("m,n,s,b,n_outer", [(1500, 45, 5, 24, 4), (1000, 300, 3, 64, 3), (600, 20, 1, 32, 5)])
+def test_train_equals_outer_steps_fp32(m, n, s, b, n_outer):
+    import torch
+    X, y = _data("logistic", m, n, seed=m)
+    h = B.CASGD(torch_dev(X), torch_dev(y), "logistic", "fp32")
+    w_pipe = torch_dev(synth.make_uniform((n,), seed=4, lo=-0.2, hi=0.2))
+    w_step = w_pipe.clone()
+    h.train(s, b, 0.4, 3, 0, n_outer, w_pipe)
+    got = {k: h.export(k) for k in EXPORTS}
+    for k in range(n_outer):
+        h.outer_step(s, b, 0.4, O.step_seed(3, k), w_step)
+    torch.cuda.synchronize()
+    assert torch.equal(w_pipe, w_step)
+    for k in EXPORTS:
+        assert np.array_equal(got[k], h.export(k)), k
+
+
 def test_train_then_steps_interleave():
     import torch
     name = "logistic-4096x64"
