@@ -37,6 +37,7 @@ int hip_fail(hipError_t e, const char* what) {
 
 constexpr int kMaxSB = 16384;
 constexpr int kPipeGatherWgs = 64;  // gather workgroups of a pipelined step launch
+constexpr int kMarginRows = 8;      // rows per margin workgroup of a pipelined step launch
 
 struct EventPair {
   hipEvent_t start = nullptr;
@@ -148,9 +149,9 @@ int ensure_workspace(casgd_ctx* h, int s, int b) {
   }
   ok = ok && grab(h->v, sizeof(float) * new_sb) && grab(h->z, sizeof(float) * new_sb) &&
        grab(h->r, sizeof(float) * new_sb) && grab(h->idx_user, sizeof(int32_t) * new_sb) &&
-       grab(h->xbuf, sizeof(unsigned long long) * casgd::kChainMaxWorkgroups * new_sb);
+       grab(h->xbuf, sizeof(unsigned long long) * (casgd::kChainMaxWorkgroups + 1) * new_sb);
   if (ok) {
-    ok = hipMemset(h->xbuf, 0, sizeof(unsigned long long) * casgd::kChainMaxWorkgroups * new_sb) ==
+    ok = hipMemset(h->xbuf, 0, sizeof(unsigned long long) * (casgd::kChainMaxWorkgroups + 1) * new_sb) ==
              hipSuccess &&
          hipDeviceSynchronize() == hipSuccess;
   }
@@ -336,6 +337,7 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
   if (e != hipSuccess) return hip_fail(e, "pipeline prologue");
 
   const int Q = casgd::chain_workgroups(s, b);
+  const bool fast = casgd::chain_fast(s, b, Q, h->ld);
   const int64_t cpr = h->ld / (h->storage == CASGD_BF16 ? 8 : 4);  // 16-byte chunks per row
   const int gs = casgd::gather::group_size(cpr);
   const int rows_per_wg = 256 / gs;
@@ -361,7 +363,18 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
     a.epoch = ++h->epoch == 0 ? ++h->epoch : h->epoch;
     a.status = h->status;
     a.preload = 0;
-    p.gram0 = (Q + casgd::kXcds - 1) / casgd::kXcds * casgd::kXcds;
+    // margins by their own workgroups (kMarginRows rows each) when the chain
+    // takes them from the exchange buffer's last s*b words
+    int next = (Q + casgd::kXcds - 1) / casgd::kXcds * casgd::kXcds;
+    if (fast) {
+      p.vbox_out = h->xbuf + static_cast<int64_t>(casgd::kChainMaxWorkgroups) * sb;
+      a.vbox = p.vbox_out;
+      p.mar0 = next;
+      p.mar_rows = kMarginRows;
+      p.mar_wgs = (sb + kMarginRows - 1) / kMarginRows;
+      next = (p.mar0 + p.mar_wgs + casgd::kXcds - 1) / casgd::kXcds * casgd::kXcds;
+    }
+    p.gram0 = next;
     if (i + 1 < n && plan.tiles > 0) {
       const StepBuffers& N = h->buf[(i + 1) % 3];
       p.gram_slots = plan.slots;

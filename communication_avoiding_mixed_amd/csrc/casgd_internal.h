@@ -81,7 +81,13 @@ struct ChainArgs {
   uint32_t epoch;            // distinct per launch on this exchange buffer
   int* status;               // bit 0 set if an exchange wait expired
   int preload;               // set by launch_chain: own rows of G staged in LDS
+  // Margins as tagged words (epoch, float) at vbox[row], written by other
+  // workgroups of the same launch; nullptr: the chain computes them itself.
+  const unsigned long long* vbox = nullptr;
 };
+// Whether chain workgroups of shape (s, b, Q, ld) run the fast recurrence
+// (the only one that can take its margins from vbox).
+bool chain_fast(int s, int b, int Q, int64_t ld);
 size_t chain_lds_bytes(int s, int b, int Q, int64_t ld);
 int chain_workgroups(int s, int b);
 constexpr int kChainMaxWorkgroups = 64;
@@ -89,13 +95,17 @@ hipError_t launch_chain(int storage, int loss, const ChainArgs& a, hipStream_t s
                         const LaunchTimer& tm = {});
 
 // One launch of the pipelined training loop: the chain of
-// outer step k on workgroups [0, a.Q), the Gram of step k+1 (gram_slots > 0)
+// outer step k on workgroups [0, a.Q), the margins of step k on
+// [mar0, mar0 + mar_wgs) (mar_wgs > 0; handed to the chain through a.vbox),
+// the Gram of step k+1 (gram_slots > 0)
 // on [gram0, gram0 + gram_slots) with gram0 a multiple of kXcds, and the
 // sample + gather of step k+2 (gath_wgs > 0) on [gath0, gath0 + gath_wgs).
 // The three roles use disjoint buffers; Y/G/yB of the chain, Y/G of the Gram
 // and idx/Y/yB of the gather belong to three different steps.
 struct PipeArgs {
   ChainArgs a;
+  int mar0 = 0, mar_wgs = 0, mar_rows = 0;  // margins: mar_rows rows per workgroup, into a.vbox
+  unsigned long long* vbox_out = nullptr;   // = a.vbox, writable
   int gram0 = 0, gram_slots = 0, tps = 0;
   const void* gY = nullptr;  // Y of step k+1 (stored type)
   float* gG = nullptr;           // G of step k+1

@@ -182,7 +182,7 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
   const int s = a.s, b = a.b, Q = a.Q, sb = s * b;
   const int q = x.q, nown = x.nown, nown_max = x.nown_max, lane = x.lane;
   float* rs = x.rs;
-  const float* vown = x.vown;
+  const float* vown = x.vown;  // (wave 0 fills it first when a.vbox is set)
   const float* yown = x.yown;
   float* acc = x.acc;
   int& abort_flag = *x.abort_flag;
@@ -209,6 +209,16 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
   const bool upd = per <= 64 && rpl <= kUpdRows;
   const int nf = upd ? kWaves - 2 : kWaves - 1;  // fold waves
   if (wv == 0) {
+    if (a.vbox) {
+      // margins of the own rows, from the launch's margin workgroups (they
+      // finish together, so all are taken at once; only this wave uses them)
+      float* vw = x.vown;
+      for (int p = lane; p < s * nown; p += 64) {
+        const int j = p / nown, t = p - (p / nown) * nown;
+        vw[j * nown_max + t] = chain::take(&a.vbox[static_cast<int64_t>(j) * b + q + Q * t], a.epoch, a.status,
+                                           &abort_flag, 0);
+      }
+    }
     float rp[CP];
 #pragma unroll
     for (int u = 0; u < CP; ++u) rp[u] = 0.f;
@@ -560,7 +570,9 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
     auto more = [&] {
       if (T4 > 0) gp.issue<kGB>(tmp, threadIdx.x, kThreads);
     };
-    if (L.wl_len > 0)
+    if (a.vbox)
+      more();  // margins are computed by other workgroups of the launch
+    else if (L.wl_len > 0)
       margins_wlds<T>(Y, a.ld, a.n, a.w, nrows, row_of, out, sm + L.wl, more);
     else
       chain::margins<T>(Y, a.ld, a.n, a.w, nrows, row_of, out, wave, lane, more);
@@ -698,12 +710,37 @@ __device__ __forceinline__ void pipe_gather(const PipeArgs& p, int g) {
 
 // T = uint16_t: bf16 storage, Gram on MFMA with (BK, D) stages; T = float:
 // float32 storage, Gram on the vector ALUs (BK, D unused).
+// Margins of rows [m * mar_rows, (m+1) * mar_rows) of step k for the chain
+// workgroups: each value goes out as a tagged word to vbox[row] (and to v).
+template <typename T>
+__device__ __forceinline__ void pipe_margins(const PipeArgs& p, int m, float* sm) {
+  const ChainArgs& a = p.a;
+  const int sb = a.s * a.b;
+  const int r0 = m * p.mar_rows;
+  const int nrows = sb - r0 < p.mar_rows ? sb - r0 : p.mar_rows;
+  if (nrows <= 0) return;
+  auto row_of = [&](int i) { return static_cast<int64_t>(r0 + i); };
+  auto out = [&](int, int64_t row, float v) {
+    chain::put(&p.vbox_out[row], tagged(a.epoch, v));
+    a.v[row] = v;
+  };
+  const T* Y = static_cast<const T*>(a.Y);
+  if (a.ld <= kWlMax)
+    margins_wlds<T>(Y, a.ld, a.n, a.w, nrows, row_of, out, sm, [] {});
+  else
+    chain::margins<T>(Y, a.ld, a.n, a.w, nrows, row_of, out, threadIdx.x >> 6, threadIdx.x & 63);
+}
+
 template <typename T, int LOSS, int BK, int D>
 __global__ __launch_bounds__(kThreads) void pipe_kernel(PipeArgs p) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   const int w = blockIdx.x;
   if (w < p.a.Q) {
     chain_body<T, LOSS>(p.a, w);
+    return;
+  }
+  if (w >= p.mar0 && w < p.mar0 + p.mar_wgs) {
+    pipe_margins<T>(p, w - p.mar0, sm);
     return;
   }
   if (w >= p.gram0 && w < p.gram0 + p.gram_slots) {
@@ -774,6 +811,10 @@ bool chain_preload(int s, int b, int Q, int64_t ld) {
   return static_cast<size_t>(chain_layout(s, b, Q, ld, true).total) * sizeof(float) <= kLdsBudget;
 }
 
+bool chain_fast(int s, int b, int Q, int64_t ld) {
+  return chain_layout(s, b, Q, ld, chain_preload(s, b, Q, ld)).acc_len > 0;
+}
+
 size_t chain_lds_bytes(int s, int b, int Q, int64_t ld) {
   const size_t need = static_cast<size_t>(chain_layout(s, b, Q, ld, chain_preload(s, b, Q, ld)).total) * sizeof(float);
   return need > kLdsReserve ? need : kLdsReserve;
@@ -806,7 +847,10 @@ hipError_t launch_pipe(int storage, int loss, const PipeArgs& p_in, hipStream_t 
   const size_t glds = storage != kStoreBF16 ? sizeof(float) * gram::kF32LdsElems
                       : sizeof(uint16_t) * (gram_variant(p.a.ld) == 0 ? gram::lds_elems<32>() : gram::lds_elems<64>());
   if (glds > lds) lds = glds;
-  const int grid = p.gath_wgs > 0 ? p.gath0 + p.gath_wgs : (p.gram_slots > 0 ? p.gram0 + p.gram_slots : p.a.Q);
+  int grid = p.a.Q;
+  if (p.mar_wgs > 0) grid = p.mar0 + p.mar_wgs;
+  if (p.gram_slots > 0) grid = p.gram0 + p.gram_slots;
+  if (p.gath_wgs > 0) grid = p.gath0 + p.gath_wgs;
   if (loss == kLogistic) return pipe_l<kLogistic>(storage, p, grid, lds, st, tm);
   if (loss == kSquared) return pipe_l<kSquared>(storage, p, grid, lds, st, tm);
   return pipe_l<kPoisson>(storage, p, grid, lds, st, tm);
