@@ -170,12 +170,12 @@ constexpr int kUpdRows = 4;  // rows per lane per block the update wave prefetch
 // waves fold each block t of r into the per-lane partial sums of the rows of
 // blocks k >= t+2 while wave 0 waits for the next block, so
 //   z_j = v_j - c * sum_lanes(acc_j + G_{j,j-1} r_{j-1}).
-// When the workgroup's column slice of w allows (at most 64 chunks, at most
-// kUpdRows rows per lane per block), wave 3 accumulates the update
-// Y^T r of its columns block by block as r arrives (the rows of the next
-// block prefetched), reduces over its lanes and writes w: then the waves
-// that fold are 1 and 2 and the function returns true.  Otherwise waves 1..3
-// fold and the caller runs the update afterwards.
+// Waves 1..3 fold (block k to wave 1 + k mod 3).  When the workgroup's column
+// slice of w allows (at most 64 chunks, at most kUpdRows rows per lane per
+// block), wave 3 also accumulates the update Y^T r of its columns block by
+// block as r arrives (the rows of the next block prefetched), reduces over
+// its lanes and writes w, and the function returns true; otherwise the
+// caller runs the update afterwards.
 template <typename T, int LOSS, int NO, int CP>
 __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
   const ChainArgs& a = *x.a;
@@ -207,7 +207,7 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
   const int rgw = 64 / cw;
   const int rpl = (b + rgw - 1) / rgw;
   const bool upd = per <= 64 && rpl <= kUpdRows;
-  const int nf = upd ? kWaves - 2 : kWaves - 1;  // fold waves
+  const int nf = kWaves - 1;  // fold waves
   if (wv == 0) {
     if (a.vbox) {
       // margins of the own rows, from the launch's margin workgroups (they
@@ -252,7 +252,6 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
             rs[jb - b + l] = rp[u];
           }
         }
-        if (abort_flag) break;
         lds_publish(&r_ready, j);
         if (!acc_now) {
           if (!lds_wait(ready, j - 1, &abort_flag, a.status)) break;
@@ -284,6 +283,9 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
           a.r[row] = rv;
         }
       }
+      // a wait that expired ends the loop (its zero values went out with the
+      // step, but the status word reports the failure)
+      if (abort_flag) break;
     }
     // the last block's r, for the update
     if (!abort_flag) {
@@ -291,13 +293,12 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
       for (int l = lane; l < b; l += 64) rs[jb + l] = chain::take(&mbox[jb + l], a.epoch, a.status, &abort_flag, 0);
       if (!abort_flag) lds_publish(&r_ready, s);
     }
-  } else if (wv <= nf) {
-    // fold wave h = wv - 1 owns the rows of the blocks k = h (mod nf); after
+  } else {
+    // fold wave h = wv - 1 owns the rows of the blocks k = h (mod 3); after
     // r of block tb is in, it folds G_{k,tb} r_tb into their partial sums
     // for every k >= tb + 2, two blocks at a time with all loads issued first
     const int h = wv - 1;
-    for (int tb = 0; tb + 2 < s; ++tb) {
-      if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status)) break;
+    auto fold = [&](int tb) {
       float rr[CP];
 #pragma unroll
       for (int u = 0; u < CP; ++u) {
@@ -335,64 +336,72 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
         }
       }
       lds_publish(&acc_ready[h], tb + 1);
-    }
-  } else if (upd) {
-    // update wave: this workgroup's chunks [ch0, ch1) of w; lane = (rgl, cl)
-    // sums rows rgl, rgl + rgw, ... of every block for chunk ch0 + cl
-    const int64_t ch0 = static_cast<int64_t>(q) * per;
-    const int64_t ch1 = ch0 + per < cpr ? ch0 + per : cpr;
-    const int cl = lane % cw, rgl = lane / cw;
-    const int64_t ch = ch0 + cl;
-    const bool col_ok = ch < ch1;
-    const u32x4* Y4 = reinterpret_cast<const u32x4*>(a.Y);
-    float accw[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) accw[e] = 0.f;
-    // rows of block tb (clamped to the last block) for this lane, unconditional loads
-    auto load_blk = [&](int tb, u32x4 (&dst)[kUpdRows]) {
-      const int tbc = tb < s ? tb : s - 1;
-#pragma unroll
-      for (int i = 0; i < kUpdRows; ++i) {
-        const int rl = rgl + rgw * i;
-        const bool ok = i < rpl && rl < b && col_ok;
-        dst[i] = Y4[(ok ? static_cast<int64_t>(tbc) * b + rl : 0) * cpr + (ok ? ch : 0)];
-      }
     };
-    auto use_blk = [&](int tb, const u32x4 (&src)[kUpdRows]) -> bool {
-      if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status)) return false;
+    if (!(upd && wv == kWaves - 1)) {
+      for (int tb = 0; tb + 2 < s; ++tb) {
+        if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status)) break;
+        fold(tb);
+      }
+    } else {
+      // the last wave also accumulates the update of this workgroup's chunks
+      // [ch0, ch1) of w: lane = (rgl, cl) sums rows rgl, rgl + rgw, ... of
+      // every block for chunk ch0 + cl, right after folding the block
+      const int64_t ch0 = static_cast<int64_t>(q) * per;
+      const int64_t ch1 = ch0 + per < cpr ? ch0 + per : cpr;
+      const int cl = lane % cw, rgl = lane / cw;
+      const int64_t ch = ch0 + cl;
+      const bool col_ok = ch < ch1;
+      const u32x4* Y4 = reinterpret_cast<const u32x4*>(a.Y);
+      float accw[E];
 #pragma unroll
-      for (int i = 0; i < kUpdRows; ++i) {
-        const int rl = rgl + rgw * i;
-        if (i < rpl && rl < b && col_ok) {
-          const float rr = rs[tb * b + rl];
-          float f[E];
-          Elems<T>::widen(src[i], f);
+      for (int e = 0; e < E; ++e) accw[e] = 0.f;
+      // rows of block tb (clamped to the last block) for this lane, unconditional loads
+      auto load_blk = [&](int tb, u32x4 (&dst)[kUpdRows]) {
+        const int tbc = tb < s ? tb : s - 1;
 #pragma unroll
-          for (int e = 0; e < E; ++e) accw[e] = fmaf(f[e], rr, accw[e]);
+        for (int i = 0; i < kUpdRows; ++i) {
+          const int rl = rgl + rgw * i;
+          const bool ok = i < rpl && rl < b && col_ok;
+          dst[i] = Y4[(ok ? static_cast<int64_t>(tbc) * b + rl : 0) * cpr + (ok ? ch : 0)];
         }
+      };
+      auto step = [&](int tb, const u32x4 (&src)[kUpdRows]) -> bool {
+        if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status)) return false;
+        if (tb + 2 < s) fold(tb);
+#pragma unroll
+        for (int i = 0; i < kUpdRows; ++i) {
+          const int rl = rgl + rgw * i;
+          if (i < rpl && rl < b && col_ok) {
+            const float rr = rs[tb * b + rl];
+            float f[E];
+            Elems<T>::widen(src[i], f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) accw[e] = fmaf(f[e], rr, accw[e]);
+          }
+        }
+        return true;
+      };
+      u32x4 ya[kUpdRows], yb[kUpdRows];
+      load_blk(0, ya);
+      bool ok = true;
+      for (int tb = 0; tb < s; tb += 2) {
+        load_blk(tb + 1, yb);
+        ok = step(tb, ya);
+        if (!ok || tb + 1 >= s) break;
+        load_blk(tb + 2, ya);
+        ok = step(tb + 1, yb);
+        if (!ok) break;
       }
-      return true;
-    };
-    u32x4 ya[kUpdRows], yb[kUpdRows];
-    load_blk(0, ya);
-    bool ok = true;
-    for (int tb = 0; tb < s; tb += 2) {
-      load_blk(tb + 1, yb);
-      ok = use_blk(tb, ya);
-      if (!ok || tb + 1 >= s) break;
-      load_blk(tb + 2, ya);
-      ok = use_blk(tb + 1, yb);
-      if (!ok) break;
-    }
-    if (ok) {
-      for (int off = cw; off < 64; off <<= 1)
+      if (ok) {
+        for (int off = cw; off < 64; off <<= 1)
 #pragma unroll
-        for (int e = 0; e < E; ++e) accw[e] += __shfl_xor(accw[e], off, 64);
-      if (rgl == 0 && col_ok) {
+          for (int e = 0; e < E; ++e) accw[e] += __shfl_xor(accw[e], off, 64);
+        if (rgl == 0 && col_ok) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int64_t col = ch * E + e;
-          if (col < a.n) a.w[col] = a.w[col] - a.c * accw[e];
+          for (int e = 0; e < E; ++e) {
+            const int64_t col = ch * E + e;
+            if (col < a.n) a.w[col] = a.w[col] - a.c * accw[e];
+          }
         }
       }
     }
