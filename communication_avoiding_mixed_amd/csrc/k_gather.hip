@@ -11,27 +11,56 @@ namespace casgd {
 namespace {
 
 // ---------------------------------------------------------------------------
-// X (float32, m x n) -> Xs (m x ld).  One thread per 16-byte output chunk.
+// X (float32, m x n) -> Xs (m x ld).  One thread per 16-byte output chunk
+// (8 elements), kSU chunks per thread per pass with every load issued before
+// the first conversion.  VEC (n a multiple of 4, so every row starts on a
+// 16-byte boundary): two 16-byte loads per chunk; the second half of a chunk
+// that ends past n reads the chunk's first half again and is zeroed.
+// Otherwise element loads with clamped addresses.
 // ---------------------------------------------------------------------------
+constexpr int kSU = 4;
+
+template <bool VEC>
 __global__ __launch_bounds__(256) void store_bf16_kernel(const float* __restrict__ X,
                                                          uint16_t* __restrict__ Xs, int64_t m,
                                                          int64_t n, int64_t ld) {
   const int64_t cpr = ld / 8;  // chunks per row
   const int64_t total = m * cpr;
-  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
-       g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t row = g / cpr;
-    const int64_t c0 = (g - row * cpr) * 8;
-    const float* src = X + row * n;
-    uint32_t packed[4];
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t g0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g0 < total;
+       g0 += stride * kSU) {
+    float v[kSU][8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t c = c0 + 2 * e;
-      const uint32_t lo = c < n ? f32_to_bf16(src[c]) : 0u;
-      const uint32_t hi = c + 1 < n ? f32_to_bf16(src[c + 1]) : 0u;
-      packed[e] = lo | (hi << 16);
+    for (int u = 0; u < kSU; ++u) {
+      const int64_t g = g0 + stride * u < total ? g0 + stride * u : g0;
+      const int64_t row = g / cpr;
+      const int64_t c0 = (g - row * cpr) * 8;
+      const float* src = X + row * n;
+      if constexpr (VEC) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src + (c0 < n ? c0 : 0));
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + (c0 + 4 < n ? c0 + 4 : 0));
+        v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+        v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = src[c0 + e < n ? c0 + e : n - 1];
+      }
     }
-    *reinterpret_cast<uint4*>(Xs + row * ld + c0) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+#pragma unroll
+    for (int u = 0; u < kSU; ++u) {
+      const int64_t g = g0 + stride * u;
+      if (g >= total) break;
+      const int64_t row = g / cpr;
+      const int64_t c0 = (g - row * cpr) * 8;
+      uint32_t packed[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = c0 + 2 * e < n ? f32_to_bf16(v[u][2 * e]) : 0u;
+        const uint32_t hi = c0 + 2 * e + 1 < n ? f32_to_bf16(v[u][2 * e + 1]) : 0u;
+        packed[e] = lo | (hi << 16);
+      }
+      *reinterpret_cast<u32x4*>(Xs + row * ld + c0) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    }
   }
 }
 
@@ -81,10 +110,14 @@ hipError_t gather_t(const void* Xs, const float* y, int64_t m, int64_t cpr, int 
 hipError_t launch_store(int storage, const float* X, void* Xs, int64_t m, int64_t n, int64_t ld,
                         hipStream_t st) {
   const int64_t chunks = m * (ld / (storage == kStoreBF16 ? 8 : 4));
-  const int64_t want = (chunks + 255) / 256;
-  const int grid = static_cast<int>(want < 65536 ? (want > 0 ? want : 1) : 65536);
-  if (storage == kStoreBF16)
-    store_bf16_kernel<<<grid, 256, 0, st>>>(X, static_cast<uint16_t*>(Xs), m, n, ld);
+  const int64_t want = (chunks + 256 * kSU - 1) / (256 * kSU);
+  const int grid = static_cast<int>(want < (1 << 20) ? (want > 0 ? want : 1) : (1 << 20));
+  if (storage == kStoreBF16) {
+    if (n % 4 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0)
+      store_bf16_kernel<true><<<grid, 256, 0, st>>>(X, static_cast<uint16_t*>(Xs), m, n, ld);
+    else
+      store_bf16_kernel<false><<<grid, 256, 0, st>>>(X, static_cast<uint16_t*>(Xs), m, n, ld);
+  }
   else
     store_f32_kernel<<<grid, 256, 0, st>>>(X, static_cast<float*>(Xs), m, n, ld);
   return hipGetLastError();

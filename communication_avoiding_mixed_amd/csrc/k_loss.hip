@@ -34,33 +34,72 @@ struct Widen<float> {
   }
 };
 
-// Grid-stride over rows; a group of GS lanes per row.  Each block writes one
-// float64 partial sum.
-template <typename T, int LOSS, int GS>
+// Grid-stride over pairs of rows; a group of GS lanes per row, R = 2 rows per
+// group at a time.  w is staged in LDS (zero past n), so the dot products
+// need no bounds checks and every row chunk of a pass is loaded before any is
+// used (kU chunks per lane per row, clamped addresses, zeroed when used).
+// Each block writes one float64 partial sum.
+constexpr int kU = 4;
+constexpr int64_t kLossWlMax = 8192;  // floats of w staged in LDS
+
+template <typename T, int LOSS, int GS, bool WLDS>
 __global__ __launch_bounds__(256) void loss_kernel(const T* __restrict__ Xs,
                                                    const float* __restrict__ y, int64_t m,
                                                    int64_t n, int64_t ld,
                                                    const float* __restrict__ w,
                                                    double* __restrict__ partial) {
   constexpr int E = Widen<T>::kElems;
+  constexpr int R = 2;
+  __shared__ __attribute__((aligned(16))) float wl[WLDS ? kLossWlMax : 4];
   const int lane = threadIdx.x % GS;
   const int64_t groups = static_cast<int64_t>(gridDim.x) * (256 / GS);
   const int64_t cpr = ld / E;
+  if constexpr (WLDS) {
+    for (int64_t c = threadIdx.x; c < ld; c += 256) wl[c] = c < n ? w[c] : 0.f;
+    __syncthreads();
+  }
+  auto wval = [&](int64_t col) -> float {
+    if constexpr (WLDS) return wl[col];
+    else return col < n ? w[col] : 0.f;
+  };
   double acc = 0.0;
-  for (int64_t row = static_cast<int64_t>(blockIdx.x) * (256 / GS) + threadIdx.x / GS; row < m;
-       row += groups) {
-    const u32x4* xr = reinterpret_cast<const u32x4*>(Xs + row * ld);
-    float d = 0.f;
-    for (int64_t c = lane; c < cpr; c += GS) {
-      float f[E];
-      Widen<T>::run(xr[c], f);
-      const int64_t col0 = c * E;
+  for (int64_t row0 = (static_cast<int64_t>(blockIdx.x) * (256 / GS) + threadIdx.x / GS) * R; row0 < m;
+       row0 += groups * R) {
+    float d[R] = {};
+    for (int64_t c0 = lane; c0 < cpr; c0 += GS * kU) {
+      u32x4 q[R][kU];
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (col0 + e < n) d = fmaf(f[e], w[col0 + e], d);
+      for (int r = 0; r < R; ++r) {
+        const int64_t row = row0 + r < m ? row0 + r : row0;
+        const u32x4* xr = reinterpret_cast<const u32x4*>(Xs + row * ld);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int64_t c = c0 + GS * u;
+          q[r][u] = xr[c < cpr ? c : 0];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t c = c0 + GS * u;
+        if (c >= cpr) break;
+        float wv[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) wv[e] = wval(c * E + e);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float f[E];
+          Widen<T>::run(q[r][u], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) d[r] = fmaf(f[e], wv[e], d[r]);
+        }
+      }
     }
-    d = group_sum<GS>(d);
-    if (lane == 0) acc += loss_value<LOSS>(static_cast<double>(d), static_cast<double>(y[row]));
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float tot = group_sum<GS>(d[r]);
+      if (lane == 0 && row0 + r < m)
+        acc += loss_value<LOSS>(static_cast<double>(tot), static_cast<double>(y[row0 + r]));
+    }
   }
   __shared__ double red[256];
   red[threadIdx.x] = acc;
@@ -86,21 +125,30 @@ __global__ __launch_bounds__(256) void loss_finish_kernel(const double* __restri
   if (threadIdx.x == 0) out[0] = red[0] * inv_m;
 }
 
+template <typename T, int LOSS, int GS>
+void loss_g(const T* X, const float* y, int64_t m, int64_t n, int64_t ld, const float* w, double* partial,
+            hipStream_t st) {
+  if (ld <= kLossWlMax)
+    loss_kernel<T, LOSS, GS, true><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+  else
+    loss_kernel<T, LOSS, GS, false><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+}
+
 template <typename T, int LOSS>
 void loss_gs(const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld, const float* w,
              double* partial, hipStream_t st) {
   const int64_t cpr = ld / Widen<T>::kElems;
   const T* X = static_cast<const T*>(Xs);
   if (cpr >= 64)
-    loss_kernel<T, LOSS, 64><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+    loss_g<T, LOSS, 64>(X, y, m, n, ld, w, partial, st);
   else if (cpr >= 32)
-    loss_kernel<T, LOSS, 32><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+    loss_g<T, LOSS, 32>(X, y, m, n, ld, w, partial, st);
   else if (cpr >= 16)
-    loss_kernel<T, LOSS, 16><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+    loss_g<T, LOSS, 16>(X, y, m, n, ld, w, partial, st);
   else if (cpr >= 8)
-    loss_kernel<T, LOSS, 8><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+    loss_g<T, LOSS, 8>(X, y, m, n, ld, w, partial, st);
   else
-    loss_kernel<T, LOSS, 4><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+    loss_g<T, LOSS, 4>(X, y, m, n, ld, w, partial, st);
 }
 
 template <typename T>
