@@ -20,6 +20,7 @@
 #include "casgd.h"
 #include "casgd_device.h"
 #include "casgd_gather.h"
+#include "casgd_chain.h"
 #include "casgd_internal.h"
 
 namespace {
@@ -80,6 +81,7 @@ struct casgd_ctx {
   double* loss_out = nullptr;
   uint32_t epoch = 0;
   int recurrence = 0;  // CASGD_OPT_RECURRENCE
+  long spin = 0;       // CASGD_OPT_SPIN_LIMIT (0: the default bound)
 
   int next_buf = 0;
   int last_buf = 0;
@@ -279,6 +281,7 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   a.xbuf = h->xbuf;
   a.epoch = ++h->epoch == 0 ? ++h->epoch : h->epoch;
   a.status = h->status;
+  a.spin = h->spin > 0 ? h->spin : casgd::chain::kSpinLimit;
   // The all-to-all kernel is the faster one on every measured shape, so it is
   // the default; the lookahead form runs only when asked for.
   const casgd::LaPlan la = h->recurrence == 2 ? casgd::la_plan(s, b) : casgd::LaPlan{};
@@ -362,6 +365,7 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
     a.xbuf = h->xbuf;
     a.epoch = ++h->epoch == 0 ? ++h->epoch : h->epoch;
     a.status = h->status;
+    a.spin = h->spin > 0 ? h->spin : casgd::chain::kSpinLimit;
     a.preload = 0;
     // margins by their own workgroups (kMarginRows rows each) when the chain
     // takes them from the exchange buffer's last s*b words
@@ -520,6 +524,10 @@ int casgd_set_option(casgd_handle h, int option, int value) {
   if (!h) return fail(CASGD_EINVAL, "NULL handle");
   if (option == CASGD_OPT_RECURRENCE && value >= 0 && value <= 2) {
     h->recurrence = value;
+    return CASGD_OK;
+  }
+  if (option == CASGD_OPT_SPIN_LIMIT && value >= 0) {
+    h->spin = value;
     return CASGD_OK;
   }
   return fail(CASGD_EINVAL, "unknown option or value");

@@ -12,7 +12,7 @@ namespace chain {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr long kSpinLimit = 1L << 22;  // polls: seconds, far above any real wait
+constexpr long kSpinLimit = 1L << 22;  // default poll bound: seconds, far above any real wait
 
 template <typename T>
 struct Elems;
@@ -49,15 +49,15 @@ __device__ __forceinline__ void put(unsigned long long* p, uint64_t word) {
   __hip_atomic_store(p, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Spin until *p carries `epoch`; returns its float.  Bounded: on expiry sets
-// *abort (LDS) and bit 0 of *status and returns 0.
+// Spin until *p carries `epoch`; returns its float.  Bounded by `limit`
+// polls: on expiry sets *abort (LDS) and bit 0 of *status and returns 0.
 __device__ __forceinline__ float take(const unsigned long long* p, uint32_t epoch, int* status,
-                                      int* abort_flag, int sleep) {
+                                      int* abort_flag, int sleep, long limit) {
   long it = 0;
   while (true) {
     const uint64_t x = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (static_cast<uint32_t>(x >> 32) == epoch) return __uint_as_float(static_cast<uint32_t>(x));
-    if (++it > kSpinLimit) {
+    if (++it > limit) {
       *abort_flag = 1;
       atomicOr(status, 1);
       return 0.f;

@@ -29,7 +29,6 @@ namespace casgd {
 namespace {
 
 using chain::Elems;
-using chain::kSpinLimit;
 using chain::kThreads;
 using chain::kWaves;
 using chain::tagged;
@@ -87,11 +86,11 @@ __host__ __device__ inline ChainLayout chain_layout(int s, int b, int Q, int64_t
 
 // Spin (bounded) until the LDS word *flag reaches `want` or the workgroup
 // aborts; false on abort or expiry.
-__device__ __forceinline__ bool lds_wait(const int* flag, int want, int* abort_flag, int* status) {
+__device__ __forceinline__ bool lds_wait(const int* flag, int want, int* abort_flag, int* status, long limit) {
   long it = 0;
   while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < want) {
     if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
-    if (++it > kSpinLimit) {
+    if (++it > limit) {
       *abort_flag = 1;
       atomicOr(status, 1);
       return false;
@@ -215,8 +214,7 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
       float* vw = x.vown;
       for (int p = lane; p < s * nown; p += 64) {
         const int j = p / nown, t = p - (p / nown) * nown;
-        vw[j * nown_max + t] = chain::take(&a.vbox[static_cast<int64_t>(j) * b + q + Q * t], a.epoch, a.status,
-                                           &abort_flag, 0);
+        vw[j * nown_max + t] = chain::take(&a.vbox[static_cast<int64_t>(j) * b + q + Q * t], a.epoch, a.status, &abort_flag, 0, a.spin);
       }
     }
     float rp[CP];
@@ -248,13 +246,13 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
         for (int u = 0; u < CP; ++u) {
           const int l = lane + 64 * u;
           if (l < b) {
-            rp[u] = chain::take(&mbox[jb - b + l], a.epoch, a.status, &abort_flag, 0);
+            rp[u] = chain::take(&mbox[jb - b + l], a.epoch, a.status, &abort_flag, 0, a.spin);
             rs[jb - b + l] = rp[u];
           }
         }
         lds_publish(&r_ready, j);
         if (!acc_now) {
-          if (!lds_wait(ready, j - 1, &abort_flag, a.status)) break;
+          if (!lds_wait(ready, j - 1, &abort_flag, a.status, a.spin)) break;
 #pragma unroll
           for (int t = 0; t < NO; ++t)
 #pragma unroll
@@ -290,7 +288,7 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
     // the last block's r, for the update
     if (!abort_flag) {
       const int jb = (s - 1) * b;
-      for (int l = lane; l < b; l += 64) rs[jb + l] = chain::take(&mbox[jb + l], a.epoch, a.status, &abort_flag, 0);
+      for (int l = lane; l < b; l += 64) rs[jb + l] = chain::take(&mbox[jb + l], a.epoch, a.status, &abort_flag, 0, a.spin);
       if (!abort_flag) lds_publish(&r_ready, s);
     }
   } else {
@@ -339,7 +337,7 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
     };
     if (!(upd && wv == kWaves - 1)) {
       for (int tb = 0; tb + 2 < s; ++tb) {
-        if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status)) break;
+        if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status, a.spin)) break;
         fold(tb);
       }
     } else {
@@ -366,7 +364,7 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
         }
       };
       auto step = [&](int tb, const u32x4 (&src)[kUpdRows]) -> bool {
-        if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status)) return false;
+        if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status, a.spin)) return false;
         if (tb + 2 < s) fold(tb);
 #pragma unroll
         for (int i = 0; i < kUpdRows; ++i) {
@@ -679,7 +677,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
           while (true) {
             x = __hip_atomic_load(&mbox[jb + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (static_cast<uint32_t>(x >> 32) == a.epoch) break;
-            if (++it > kSpinLimit) {
+            if (++it > a.spin) {
               abort_flag = 1;
               atomicOr(a.status, 1);
               break;

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void chain_la_kernel(ChainArgs a, int d, 
       const int jb = j * b;
       if (wave == 0) {
         for (int k = lane; k < b; k += 64)
-          fbuf[(j & 1) * kMaxB + k] = take(&inbox_c[jb + k], a.epoch, a.status, &abort_flag, 0);
+          fbuf[(j & 1) * kMaxB + k] = take(&inbox_c[jb + k], a.epoch, a.status, &abort_flag, 0, a.spin);
       }
       __syncthreads();
       if (abort_flag) return;
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void chain_la_kernel(ChainArgs a, int d, 
       const int tb = t * b;
       if (wave == 0) {
         for (int k = lane; k < b; k += 64)
-          rs[tb + k] = take(&inbox_h[static_cast<int64_t>(h) * sb + tb + k], a.epoch, a.status, &abort_flag, 0);
+          rs[tb + k] = take(&inbox_h[static_cast<int64_t>(h) * sb + tb + k], a.epoch, a.status, &abort_flag, 0, a.spin);
       }
       __syncthreads();
       if (abort_flag) return;
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void chain_la_kernel(ChainArgs a, int d, 
     // ----------------------------------------------------------- receiver
     red = sm + L.yb;  // unused by receivers otherwise
     for (int k = threadIdx.x; k < sb; k += kThreads) {
-      rs[k] = take(&bcast[k], a.epoch, a.status, &abort_flag, 1);
+      rs[k] = take(&bcast[k], a.epoch, a.status, &abort_flag, 1, a.spin);
       if (abort_flag) break;
     }
     __syncthreads();

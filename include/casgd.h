@@ -182,7 +182,14 @@ enum casgd_option {
    *     (taken for 16 <= b <= 64, b a multiple of 16, s >= 2; otherwise 1).
    * All forms give bit-identical results for a given shape and form; the
    * forms differ from each other only in float32 rounding order. */
-  CASGD_OPT_RECURRENCE = 0
+  CASGD_OPT_RECURRENCE = 0,
+  /* Bound, in polls, of every wait between workgroups of the recurrence
+   * (0, the default: 2^22 polls, seconds, far beyond any real wait).  For
+   * tests of the failure path: a small bound makes the waits expire, every
+   * kernel still ends, the step's results are invalid, and the next
+   * casgd_loss / casgd_debug_export / casgd_get_timing reports CASGD_EHIP
+   * (once; the error word is then cleared). */
+  CASGD_OPT_SPIN_LIMIT = 1
 };
 
 /* Set an option of the handle; later outer steps use it.  EINVAL for an

@@ -222,3 +222,37 @@ def test_side_stream_and_timing():
     # pipelined: one stand-alone Gram (the first step's), then one launch per step
     assert cnt == 5 and ms > 0
     assert g_cnt == 1 and g_ms > 0
+
+
+@pytest.mark.parametrize("rec", [B.RECURRENCE_ALL_TO_ALL, B.RECURRENCE_LOOKAHEAD])
+def test_expired_waits_are_reported_and_cleared(rec):
+    """With a bound of one poll the waits between workgroups expire: every
+    kernel still ends, the next loss call reports the failure once, and with
+    the default bound the handle gives the same results as a fresh one."""
+    import torch
+    X = synth.make_uniform((6000, 256), seed=21, lo=-0.3, hi=0.3)
+    y = _targets("logistic", 6000, 8)
+    s, b, eta = 16, 64, 0.5
+    h = B.CASGD(torch_dev(X), torch_dev(y), "logistic")
+    h.set_option(B.OPT_RECURRENCE, rec)
+    h.set_option(B.OPT_SPIN_LIMIT, 1)
+    w = torch.zeros(256, device="cuda")
+    h.outer_step(s, b, eta, 5, w)
+    with pytest.raises(B.CasgdError, match="timed out"):
+        h.loss_value(w)
+    if rec == B.RECURRENCE_ALL_TO_ALL:
+        h.train(s, b, eta, 0, 0, 3, w)  # the pipelined launches end as well
+        with pytest.raises(B.CasgdError, match="timed out"):
+            h.loss_value(w)
+    h.set_option(B.OPT_SPIN_LIMIT, 0)
+    w1 = torch.zeros(256, device="cuda")
+    h.train(s, b, eta, 0, 0, 4, w1)
+    val = h.loss_value(w1)
+    fresh = B.CASGD(torch_dev(X), torch_dev(y), "logistic")
+    fresh.set_option(B.OPT_RECURRENCE, rec)
+    w2 = torch.zeros(256, device="cuda")
+    fresh.train(s, b, eta, 0, 0, 4, w2)
+    assert torch.equal(w1, w2)
+    assert val == fresh.loss_value(w2)
+    with pytest.raises(B.CasgdError):
+        h.set_option(B.OPT_SPIN_LIMIT, -1)
