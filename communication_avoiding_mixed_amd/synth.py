@@ -139,3 +139,15 @@ def make_uniform(shape, seed: int, lo: float = -1.0, hi: float = 1.0) -> np.ndar
     """Seeded float32 values uniform in [lo, hi) for edge-case tests."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.uniform(lo, hi, size=shape).astype(np.float32)
+
+
+def make_grid(shape, seed: int, kmax: int, scale_log2: int) -> np.ndarray:
+    """Seeded float32 values k * 2^-scale_log2, k uniform in [-kmax, kmax].
+
+    Values with few significant bits: products and sums of them stay exact
+    in float32 as long as the sums stay below 2^24 grid units, so a dot
+    product comes out the same in any summation order.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    k = rng.integers(-kmax, kmax + 1, size=shape)
+    return (k.astype(np.float64) * 2.0 ** -scale_log2).astype(np.float32)

@@ -33,6 +33,8 @@ Readings taken where the page is silent (each is listed in the design notes):
   * "linear" regression uses the squared loss l = (z - y)^2 / 2.
   * no regularisation.
   * low precision = bfloat16 with round-to-nearest, ties to even.
+  * the margin vector is float32 by default; its bfloat16 form (the recipe's
+    low-precision margins) rounds each float32 margin once.
   * eta enters as the float32 value the GPU receives, widened to float64.
 
 Parity status of each function:
@@ -44,6 +46,9 @@ Parity status of each function:
   outer_step ...................... pinned (equals s plain SGD steps; s = 1;
                                      squared loss = linear solve; exact
                                      rational arithmetic; orthogonal rows)
+  stored_margins / bf16 margins ... pinned (hand-placed ties and near-ties
+                                     with known rounded values; exact s = 1
+                                     and s = 2 steps in rational arithmetic)
   full_loss / full_gradient ....... pinned (closed forms at w = 0; finite
                                      differences)
   train (many outer steps) ........ parity unpinned beyond the per-step pins
@@ -227,25 +232,45 @@ def recurrence(G: dict, v, yB, s: int, b: int, eta, loss: str):
     return z, r
 
 
-def outer_step_rows(Y, yB, w0, s: int, b: int, eta, loss: str) -> dict:
-    """One CA-SGD outer iteration on already-gathered rows Y (s*b x n)."""
+def stored_margins(v, margin: str) -> np.ndarray:
+    """The margin vector as the recurrence receives it.
+
+    The Abstract's recipe keeps the margin vector in low precision.  "fp32":
+    v is used as formed (the high-precision reading).  "bf16": v is formed at
+    float32 precision and each value is then rounded to the nearest
+    bfloat16, ties to even; the float32 step makes the rounding decision in
+    the precision the GPU takes it in, so for a v that float32 holds exactly
+    both sides round the same value.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if margin == "fp32":
+        return v
+    if margin == "bf16":
+        return bf16_to_f64(bf16_bits(v.astype(np.float32)))
+    raise ValueError(f"unknown margin precision {margin!r}")
+
+
+def outer_step_rows(Y, yB, w0, s: int, b: int, eta, loss: str, margin: str = "fp32") -> dict:
+    """One CA-SGD outer iteration on already-gathered rows Y (s*b x n).
+
+    `margin` is the stored precision of v = Y w0 (see stored_margins)."""
     w0 = np.asarray(w0, dtype=np.float64)
     c = step_size(eta, b)
     G = gram_blocks(Y, s, b)
-    v = Y @ w0
+    v = stored_margins(Y @ w0, margin)
     z, r = recurrence(G, v, yB, s, b, eta, loss)
     w = w0 - c * (Y.T @ r)
     return {"G": G, "v": v, "z": z, "r": r, "w": w}
 
 
 def outer_step(X_f32, y_f32, w0, s: int, b: int, eta, seed: int, loss: str,
-               storage: str = "bf16", idx=None) -> dict:
+               storage: str = "bf16", idx=None, margin: str = "fp32") -> dict:
     """One outer step from the full data: sample (or take idx), gather, step."""
     m = np.asarray(X_f32).shape[0]
     if idx is None:
         idx = sample_indices(seed, m, s * b)
     Y, yB = gather(X_f32, y_f32, idx, storage)
-    out = outer_step_rows(Y, yB, w0, s, b, eta, loss)
+    out = outer_step_rows(Y, yB, w0, s, b, eta, loss, margin)
     out["idx"] = np.asarray(idx, dtype=np.int64)
     out["Y"] = Y
     out["yB"] = yB
@@ -290,11 +315,11 @@ def full_gradient(X_f32, y_f32, w, loss: str, storage: str = "bf16") -> np.ndarr
 
 def train(X_f32, y_f32, w0, s: int, b: int, eta, loss: str, base_seed: int,
           n_outer: int, storage: str = "bf16", first_step: int = 0,
-          method: str = "ca") -> np.ndarray:
+          method: str = "ca", margin: str = "fp32") -> np.ndarray:
     """n_outer outer steps from w0; step k samples with step_seed(base_seed, k).
 
-    method "ca" runs the CA-SGD outer iteration, "sgd" runs s plain SGD steps
-    on the same minibatches.
+    method "ca" runs the CA-SGD outer iteration (margins stored at `margin`
+    precision), "sgd" runs s plain SGD steps on the same minibatches.
     """
     m = np.asarray(X_f32).shape[0]
     w = np.array(w0, dtype=np.float64)
@@ -302,7 +327,7 @@ def train(X_f32, y_f32, w0, s: int, b: int, eta, loss: str, base_seed: int,
         idx = sample_indices(step_seed(base_seed, k), m, s * b)
         Y, yB = gather(X_f32, y_f32, idx, storage)
         if method == "ca":
-            w = outer_step_rows(Y, yB, w, s, b, eta, loss)["w"]
+            w = outer_step_rows(Y, yB, w, s, b, eta, loss, margin)["w"]
         elif method == "sgd":
             w = sgd_steps(Y, yB, w, s, b, eta, loss)
         else:

@@ -360,3 +360,100 @@ def test_planted_mistakes_are_caught(monkeypatch):
         bad = O.outer_step_rows(Y, yB, w0, s, b, 0.7, "logistic")["w"]
         assert _rel(bad, sgd) > 1e-6, broken.__name__
         monkeypatch.undo()
+
+
+# ---------------------------------------------------------------- bf16 margins
+# bfloat16 keeps 8 significant bits: spacing 2^-7 on [1, 2), 2^-6 on [2, 4),
+# 2^-8 on [1/2, 1), 1 on [128, 256).  Every expected value is placed by hand.
+_MARGIN_CASES = [
+    (1.0 + 2.0 ** -8, 1.0),                              # tie, even neighbour below
+    (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6),              # tie, even neighbour above
+    (1.0 + 2.0 ** -8 + 2.0 ** -20, 1.0 + 2.0 ** -7),     # just above a tie
+    (1.0 + 2.0 ** -8 - 2.0 ** -20, 1.0),                 # just below a tie
+    (-(1.0 + 3 * 2.0 ** -8), -(1.0 + 2.0 ** -6)),        # sign is kept
+    (1.0 - 2.0 ** -8, 1.0 - 2.0 ** -8),                  # exact below 1
+    (2.0 + 2.0 ** -8, 2.0),                              # below the tie at 2 + 2^-7
+    (255.5, 256.0),                                      # tie, rounds up into the next binade
+    (3.0, 3.0),
+    (0.0, 0.0),
+    (2.0 ** -130, 2.0 ** -130),                          # subnormal, exact
+    # float64 value just above a tie that float32 cannot hold: the float32
+    # step lands on the tie itself, which then goes to even (the decision is
+    # taken in float32, as on the GPU)
+    (1.0 + 2.0 ** -8 + 2.0 ** -30, 1.0),
+]
+
+
+def test_bf16_margins_hand_built():
+    v = np.array([c[0] for c in _MARGIN_CASES])
+    want = np.array([c[1] for c in _MARGIN_CASES])
+    got = O.stored_margins(v, "bf16")
+    assert np.array_equal(got, want)
+    assert np.array_equal(O.stored_margins(v, "fp32"), v)
+    with pytest.raises(ValueError):
+        O.stored_margins(v, "fp16")
+
+
+def _squared_step_fractions(Yi, yq, wq, s, b, c, vhat):
+    """The squared-loss outer step in exact rationals from given margins."""
+    n = len(wq)
+    z = [None] * (s * b)
+    r = [None] * (s * b)
+    for j in range(s):
+        for i in range(j * b, (j + 1) * b):
+            acc = Fraction(0)
+            for t in range(j):
+                for k in range(t * b, (t + 1) * b):
+                    acc += sum(Yi[i][q] * Yi[k][q] for q in range(n)) * r[k]
+            z[i] = vhat[i] - c * acc
+            r[i] = z[i] - yq[i]
+    return [wq[q] - c * sum(Yi[i][q] * r[i] for i in range(s * b)) for q in range(n)]
+
+
+def test_bf16_margin_step_matches_exact_rationals():
+    # rows chosen so that Y w0 lands on ties and near-ties of bf16 (w0 = [1, 2^-8])
+    Yi = [[1, 1], [1, 3], [1, -1], [2, 1]]
+    wq = [Fraction(1), Fraction(1, 256)]
+    vhat = [Fraction(1), 1 + Fraction(1, 64), 1 - Fraction(1, 256), Fraction(2)]  # by hand
+    yq = [Fraction(1, 4), Fraction(-3, 4), Fraction(1, 2), Fraction(5, 4)]
+    s, b = 2, 2
+    c = Fraction(3, 8) / b
+    Y = np.array(Yi, np.float64)
+    yB = np.array([float(x) for x in yq])
+    w0 = np.array([float(x) for x in wq])
+    exact = np.array([float(x) for x in _squared_step_fractions(Yi, yq, wq, s, b, c, vhat)])
+    out = O.outer_step_rows(Y, yB, w0, s, b, 0.375, "squared", margin="bf16")
+    assert np.array_equal(out["v"], np.array([float(x) for x in vhat]))
+    assert _rel(out["w"], exact) <= 1e-15
+    # the same step from unrounded margins is a different answer: the pin sees the rounding
+    v_plain = [sum(Yi[i][q] * wq[q] for q in range(2)) for i in range(4)]
+    plain = np.array([float(x) for x in _squared_step_fractions(Yi, yq, wq, s, b, c, v_plain)])
+    assert _rel(plain, exact) > 1e-4
+    assert _rel(O.outer_step_rows(Y, yB, w0, s, b, 0.375, "squared")["w"], plain) <= 1e-15
+
+
+@pytest.mark.parametrize("loss", LOSSES)
+def test_bf16_margins_equal_fp32_when_margins_are_bf16_values(loss):
+    # margins that bf16 holds exactly: the two precisions give the same step
+    rng = np.random.default_rng(47)
+    s, b, n = 3, 4, 6
+    Y = rng.integers(-3, 4, (s * b, n)) / 4.0
+    w0 = rng.integers(-3, 4, n) / 8.0
+    yB = _targets(rng, s * b, loss)
+    a = O.outer_step_rows(Y, yB, w0, s, b, 0.25, loss, margin="bf16")
+    f = O.outer_step_rows(Y, yB, w0, s, b, 0.25, loss)
+    for key in ("v", "z", "r", "w"):
+        assert np.array_equal(a[key], f[key]), key
+
+
+def test_bf16_margin_training_run_stays_close_to_sgd():
+    # the recipe's claim in miniature: bf16 margins change the final loss little
+    X = (np.random.default_rng(53).standard_normal((600, 20)) / 4.0).astype(np.float32)
+    wstar = np.random.default_rng(54).standard_normal(20)
+    y = np.where(X.astype(np.float64) @ wstar >= 0, 1.0, -1.0).astype(np.float32)
+    w_sgd = O.train(X, y, np.zeros(20), 4, 8, 0.5, "logistic", 3, 30, storage="fp32", method="sgd")
+    w_mix = O.train(X, y, np.zeros(20), 4, 8, 0.5, "logistic", 3, 30, margin="bf16")
+    f_sgd = O.full_loss(X, y, w_sgd, "logistic", storage="fp32")
+    f_mix = O.full_loss(X, y, w_mix, "logistic", storage="fp32")
+    assert abs(f_mix - f_sgd) <= 5e-3 * f_sgd
+    assert not np.array_equal(w_mix, O.train(X, y, np.zeros(20), 4, 8, 0.5, "logistic", 3, 30))
