@@ -457,3 +457,55 @@ def test_bf16_margin_training_run_stays_close_to_sgd():
     f_mix = O.full_loss(X, y, w_mix, "logistic", storage="fp32")
     assert abs(f_mix - f_sgd) <= 5e-3 * f_sgd
     assert not np.array_equal(w_mix, O.train(X, y, np.zeros(20), 4, 8, 0.5, "logistic", 3, 30))
+
+
+def test_margin_choices_hand_built():
+    # v = 1 + 2^-8 sits on a boundary: both neighbours are admissible
+    Y = np.array([[1.0, 1.0], [1.0, 0.0], [1.0, 3.0]])
+    w0 = np.array([1.0, 2.0 ** -8])
+    nearest, other, amb = O.margin_choices(Y, w0)
+    assert list(amb) == [True, False, True]
+    assert nearest[0] == 1.0 and other[0] == 1.0 + 2.0 ** -7
+    assert nearest[1] == other[1] == 1.0
+    assert nearest[2] == 1.0 + 2.0 ** -6 and other[2] == 1.0 + 2.0 ** -7
+    yB = np.zeros(3)
+    with pytest.raises(ValueError):
+        O.outer_step_rows(Y, yB, w0, 1, 3, 0.5, "squared", margin="bf16",
+                          take_other=np.array([False, True, False]))
+    out = O.outer_step_rows(Y, yB, w0, 1, 3, 0.5, "squared", margin="bf16",
+                            take_other=np.array([True, False, False]))
+    assert list(out["v"]) == [1.0 + 2.0 ** -7, 1.0, 1.0 + 2.0 ** -6]
+
+
+def _f32_dot_orders(y, w, rng):
+    """float32 dot products of one row in several summation orders."""
+    p = (y.astype(np.float32) * w.astype(np.float32)).astype(np.float32)
+    out = []
+    for order in (np.arange(len(p)), np.arange(len(p))[::-1], rng.permutation(len(p))):
+        acc = np.float32(0.0)
+        for k in order:
+            acc = np.float32(acc + p[k])
+        out.append(acc)
+    q = p.copy()  # pairwise
+    while len(q) > 1:
+        if len(q) % 2:
+            q = np.append(q, np.float32(0.0))
+        q = (q[0::2] + q[1::2]).astype(np.float32)
+    out.append(q[0])
+    return out
+
+
+def test_margin_choices_cover_float32_orders():
+    import torch
+    rng = np.random.default_rng(61)
+    n = 512
+    X = (rng.standard_normal((300, n)) / np.sqrt(n)).astype(np.float32)
+    Y = O.stored_values(X, "bf16")
+    w0 = rng.standard_normal(n).astype(np.float32)
+    nearest, other, amb = O.margin_choices(Y, w0)
+    # the worst-case bound leaves most rows with a single admissible value
+    assert 0 < amb.sum() < 0.5 * len(amb)
+    for i in range(Y.shape[0]):
+        for v32 in _f32_dot_orders(Y[i], w0, rng):
+            got = float(torch.tensor([float(v32)], dtype=torch.float32).to(torch.bfloat16).to(torch.float64)[0])
+            assert got == nearest[i] or (amb[i] and got == other[i]), (i, float(v32), nearest[i], other[i])
