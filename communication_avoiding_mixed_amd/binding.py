@@ -21,7 +21,7 @@ BF16, FP32 = 0, 1
 OK, EINVAL, ENOMEM, EHIP = 0, -1, -2, -3
 EXPORT_IDX, EXPORT_Y, EXPORT_YB, EXPORT_G, EXPORT_V, EXPORT_Z, EXPORT_R = range(7)
 K_GATHER, K_GRAM, K_CHAIN, K_PIPE = range(4)
-OPT_RECURRENCE, OPT_SPIN_LIMIT = 0, 1
+OPT_RECURRENCE, OPT_SPIN_LIMIT, OPT_MARGIN_BF16 = 0, 1, 2
 RECURRENCE_AUTO, RECURRENCE_ALL_TO_ALL, RECURRENCE_LOOKAHEAD = 0, 1, 2
 KERNEL_NAMES = {K_GATHER: "gather", K_GRAM: "gram", K_CHAIN: "chain", K_PIPE: "pipe"}
 

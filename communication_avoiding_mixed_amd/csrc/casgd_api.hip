@@ -82,6 +82,7 @@ struct casgd_ctx {
   uint32_t epoch = 0;
   int recurrence = 0;  // CASGD_OPT_RECURRENCE
   long spin = 0;       // CASGD_OPT_SPIN_LIMIT (0: the default bound)
+  int margin_bf16 = 0; // CASGD_OPT_MARGIN_BF16
 
   int next_buf = 0;
   int last_buf = 0;
@@ -282,6 +283,7 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   a.epoch = ++h->epoch == 0 ? ++h->epoch : h->epoch;
   a.status = h->status;
   a.spin = h->spin > 0 ? h->spin : casgd::chain::kSpinLimit;
+  a.vround = h->margin_bf16;
   // The all-to-all kernel is the faster one on every measured shape, so it is
   // the default; the lookahead form runs only when asked for.
   const casgd::LaPlan la = h->recurrence == 2 ? casgd::la_plan(s, b) : casgd::LaPlan{};
@@ -366,6 +368,7 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
     a.epoch = ++h->epoch == 0 ? ++h->epoch : h->epoch;
     a.status = h->status;
     a.spin = h->spin > 0 ? h->spin : casgd::chain::kSpinLimit;
+    a.vround = h->margin_bf16;
     a.preload = 0;
     // margins by their own workgroups (kMarginRows rows each) when the chain
     // takes them from the exchange buffer's last s*b words
@@ -528,6 +531,10 @@ int casgd_set_option(casgd_handle h, int option, int value) {
   }
   if (option == CASGD_OPT_SPIN_LIMIT && value >= 0) {
     h->spin = value;
+    return CASGD_OK;
+  }
+  if (option == CASGD_OPT_MARGIN_BF16 && (value == 0 || value == 1)) {
+    h->margin_bf16 = value;
     return CASGD_OK;
   }
   return fail(CASGD_EINVAL, "unknown option or value");

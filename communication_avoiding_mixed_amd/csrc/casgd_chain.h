@@ -66,6 +66,12 @@ __device__ __forceinline__ float take(const unsigned long long* p, uint32_t epoc
   }
 }
 
+// A margin as the recurrence stores it: float32, or (vround) rounded to the
+// nearest bf16, ties to even, and held in a float.
+__device__ __forceinline__ float stored_margin(float v, int vround) {
+  return vround ? bf16_to_f32(f32_to_bf16(v)) : v;
+}
+
 // Margins x . w of `nrows` rows of Y, row number row_of(p) for p < nrows.
 // Each wave takes kRB rows at a time so their loads are in flight together;
 // the weights of the same columns are loaded in the same batch.  `issued()`

@@ -82,6 +82,7 @@ struct ChainArgs {
   int* status;               // bit 0 set if an exchange wait expired
   int preload;               // set by launch_chain: own rows of G staged in LDS
   long spin;                 // polls before a wait between workgroups expires
+  int vround;                // margins stored as bf16 (rounded when formed) instead of float32
   // Margins as tagged words (epoch, float) at vbox[row], written by other
   // workgroups of the same launch; nullptr: the chain computes them itself.
   const unsigned long long* vbox = nullptr;

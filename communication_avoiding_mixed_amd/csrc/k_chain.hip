@@ -571,6 +571,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
     const float ylab = a.yB[row_of(yp)];
     f32x4 tmp[kGB];
     auto out = [&](int p, int64_t row, float v) {
+      v = chain::stored_margin(v, a.vround);
       vown[slot_of(p)] = v;
       a.v[row] = v;
     };
@@ -728,6 +729,7 @@ __device__ __forceinline__ void pipe_margins(const PipeArgs& p, int m, float* sm
   if (nrows <= 0) return;
   auto row_of = [&](int i) { return static_cast<int64_t>(r0 + i); };
   auto out = [&](int, int64_t row, float v) {
+    v = chain::stored_margin(v, a.vround);
     chain::put(&p.vbox_out[row], tagged(a.epoch, v));
     a.v[row] = v;
   };

@@ -221,6 +221,7 @@ __global__ __launch_bounds__(kThreads) void chain_la_kernel(ChainArgs a, int d, 
           return static_cast<int64_t>(j) * b + h + static_cast<int64_t>(M) * (p - j * H);
         },
         [&](int p, int64_t row, float v) {
+          v = chain::stored_margin(v, a.vround);
           vown[p] = v;
           a.v[row] = v;
         },

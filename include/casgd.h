@@ -189,7 +189,16 @@ enum casgd_option {
    * kernel still ends, the step's results are invalid, and the next
    * casgd_loss / casgd_debug_export / casgd_get_timing reports CASGD_EHIP
    * (once; the error word is then cleared). */
-  CASGD_OPT_SPIN_LIMIT = 1
+  CASGD_OPT_SPIN_LIMIT = 1,
+  /* Precision of the stored margin vector v = Y w0 (Abstract of
+   * "Mixed-Precision Communication-Avoiding SGD for Generalized Linear Models
+   * on GPUs": the recipe keeps the margin vector in low precision).
+   *   0 (default) float32;
+   *   1 each margin is accumulated in float32 and rounded once to bfloat16
+   *     (nearest, ties to even) when formed; the recurrence starts from the
+   *     rounded value and CASGD_EXPORT_V returns it, widened to float.
+   * Applies to every recurrence form and to casgd_train. */
+  CASGD_OPT_MARGIN_BF16 = 2
 };
 
 /* Set an option of the handle; later outer steps use it.  EINVAL for an

@@ -49,9 +49,9 @@ Parity status of each function:
   stored_margins / bf16 margins ... pinned (hand-placed ties and near-ties
                                      with known rounded values; an exact
                                      s = 2 step in rational arithmetic)
-  margin_choices .................. pinned (hand-placed boundaries; every
-                                     float32 summation order of random rows
-                                     lands on an admissible choice)
+  margin_choices .................. pinned (hand-placed boundaries and a
+                                     cancelling row; every float32 summation
+                                     order of random rows lands in the range)
   full_loss / full_gradient ....... pinned (closed forms at w = 0; finite
                                      differences)
   train (many outer steps) ........ parity unpinned beyond the per-step pins
@@ -254,16 +254,15 @@ def stored_margins(v, margin: str) -> np.ndarray:
 
 
 def margin_choices(Y, w0):
-    """Both admissible bf16 margins of each row when v is formed in float32.
+    """The range of admissible bf16 margins when v is formed in float32.
 
     A float32 dot product of n terms, summed in any order with rounding to
     nearest, is within e = gamma_n * sum_k |y_k w_k| of the exact value
     (gamma_n = n u / (1 - n u), u = 2^-24; Higham, Accuracy and Stability of
-    Numerical Algorithms, 2nd ed., section 3.1).  Where [v - e, v + e] holds a
-    bf16 rounding boundary, the float32 value may round to either side.
-    Returns (nearest, other, ambiguous): the rounding of the exact v, the
-    neighbour on the far side of the boundary (equal to nearest where there
-    is none), and the mask of rows that have one.
+    Numerical Algorithms, 2nd ed., section 3.1), and rounding is monotone, so
+    every admissible stored margin is a bf16 value in [round(v - e),
+    round(v + e)].  Returns (nearest, lo, hi): the rounding of the exact v and
+    the two ends of that range.
     """
     Y = np.asarray(Y, dtype=np.float64)
     w0 = np.asarray(w0, dtype=np.float64)
@@ -271,46 +270,30 @@ def margin_choices(Y, w0):
     nu = Y.shape[1] * 2.0 ** -24
     # widened by the float32 step that precedes each rounding below
     e = nu / (1.0 - nu) * (np.abs(Y) @ np.abs(w0)) + 2.0 ** -23 * np.abs(v)
-    nearest = stored_margins(v, "bf16")
-    lo = stored_margins(v - e, "bf16")
-    hi = stored_margins(v + e, "bf16")
-    other = np.where(lo != nearest, lo, hi)
-    return nearest, other, other != nearest
+    return stored_margins(v, "bf16"), stored_margins(v - e, "bf16"), stored_margins(v + e, "bf16")
 
 
-def outer_step_rows(Y, yB, w0, s: int, b: int, eta, loss: str, margin: str = "fp32",
-                    take_other=None) -> dict:
+def outer_step_rows(Y, yB, w0, s: int, b: int, eta, loss: str, margin: str = "fp32") -> dict:
     """One CA-SGD outer iteration on already-gathered rows Y (s*b x n).
 
-    `margin` is the stored precision of v = Y w0 (see stored_margins).  With
-    bf16 margins, `take_other` (a boolean mask inside margin_choices'
-    ambiguous rows) selects the other admissible rounding for those rows, so
-    a result can be followed from either valid rounding decision."""
+    `margin` is the stored precision of v = Y w0 (see stored_margins)."""
     w0 = np.asarray(w0, dtype=np.float64)
     c = step_size(eta, b)
     G = gram_blocks(Y, s, b)
     v = stored_margins(Y @ w0, margin)
-    if take_other is not None:
-        if margin != "bf16":
-            raise ValueError("take_other needs bf16 margins")
-        nearest, other, ambiguous = margin_choices(Y, w0)
-        take_other = np.asarray(take_other, dtype=bool)
-        if np.any(take_other & ~ambiguous):
-            raise ValueError("take_other selects a row with a single admissible rounding")
-        v = np.where(take_other, other, nearest)
     z, r = recurrence(G, v, yB, s, b, eta, loss)
     w = w0 - c * (Y.T @ r)
     return {"G": G, "v": v, "z": z, "r": r, "w": w}
 
 
 def outer_step(X_f32, y_f32, w0, s: int, b: int, eta, seed: int, loss: str,
-               storage: str = "bf16", idx=None, margin: str = "fp32", take_other=None) -> dict:
+               storage: str = "bf16", idx=None, margin: str = "fp32") -> dict:
     """One outer step from the full data: sample (or take idx), gather, step."""
     m = np.asarray(X_f32).shape[0]
     if idx is None:
         idx = sample_indices(seed, m, s * b)
     Y, yB = gather(X_f32, y_f32, idx, storage)
-    out = outer_step_rows(Y, yB, w0, s, b, eta, loss, margin, take_other)
+    out = outer_step_rows(Y, yB, w0, s, b, eta, loss, margin)
     out["idx"] = np.asarray(idx, dtype=np.int64)
     out["Y"] = Y
     out["yB"] = yB

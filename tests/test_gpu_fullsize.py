@@ -7,6 +7,8 @@ seeded weights within relative L2 1e-4 of the oracle for G, v, z, r and w
 loss at w = 0 against its closed form and at the seeded weights against the
 oracle; and the whole run (20 or 200 outer steps from w = 0) ending within
 0.5% of the loss of float64 SGD on the float32 data over the same minibatches.
+The same step and run are repeated with bf16-stored margins (the recipe's
+low-precision margin vector), held to the same bars.
 """
 
 import math
@@ -19,7 +21,7 @@ from communication_avoiding_mixed_amd import binding as B
 from communication_avoiding_mixed_amd import synth
 from oracle import casgd_oracle as O
 
-from gpu_common import LOSS_GAP, REL_TOL, check_gram, rel_l2, torch_dev
+from gpu_common import LOSS_GAP, REL_TOL, check_bf16_margins, check_gram, rel_l2, torch_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -83,4 +85,20 @@ def test_full_size_workload(name):
           f"(start {f0:.4f}); data {t_gen:.0f}s total {time.time() - t0:.0f}s", flush=True)
     assert f_gpu < f0
     assert gap <= LOSS_GAP
+
+    # the recipe's bf16-stored margins: the same step and the same run
+    h.set_option(B.OPT_MARGIN_BF16, 1)
+    w = torch_dev(w0)
+    h.outer_step(wl.s, wl.b, wl.eta, seed, w)
+    merrs, flips = check_bf16_margins(h, ref["Y"], ref["yB"], w0, wl.s, wl.b, wl.eta, wl.loss,
+                                      w.cpu().numpy())
+    for k, (e, bar) in merrs.items():
+        assert e <= bar, ("bf16 margins", k, e, bar, flips)
+    wm = torch.zeros(wl.n, device="cuda")
+    h.train(wl.s, wl.b, wl.eta, 0, 0, wl.outer, wm)
+    f_mix = h.loss_value(wm)
+    gap_mix = abs(f_mix - f_ref) / abs(f_ref)
+    print(f"{name}: bf16 margins: step {({k: f'{e:.1e}/{bar:.1e}' for k, (e, bar) in merrs.items()})} "
+          f"({flips} rows off the nearest rounding), final loss {f_mix:.6f} gap {gap_mix:.2e}", flush=True)
+    assert gap_mix <= LOSS_GAP
     h.close()

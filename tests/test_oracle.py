@@ -460,21 +460,21 @@ def test_bf16_margin_training_run_stays_close_to_sgd():
 
 
 def test_margin_choices_hand_built():
-    # v = 1 + 2^-8 sits on a boundary: both neighbours are admissible
-    Y = np.array([[1.0, 1.0], [1.0, 0.0], [1.0, 3.0]])
+    # v = 1 + 2^-8 and 1 + 3 * 2^-8 sit on boundaries: both neighbours admissible;
+    # v = 1 has a single admissible value; the cancelling last row has
+    # v = 2^-20 against sum |y w| of about 2, so its range spans many bf16 values
+    Y = np.array([[1.0, 1.0], [1.0, 0.0], [1.0, 3.0], [1.0, -1.0]])
     w0 = np.array([1.0, 2.0 ** -8])
-    nearest, other, amb = O.margin_choices(Y, w0)
-    assert list(amb) == [True, False, True]
-    assert nearest[0] == 1.0 and other[0] == 1.0 + 2.0 ** -7
-    assert nearest[1] == other[1] == 1.0
-    assert nearest[2] == 1.0 + 2.0 ** -6 and other[2] == 1.0 + 2.0 ** -7
-    yB = np.zeros(3)
-    with pytest.raises(ValueError):
-        O.outer_step_rows(Y, yB, w0, 1, 3, 0.5, "squared", margin="bf16",
-                          take_other=np.array([False, True, False]))
-    out = O.outer_step_rows(Y, yB, w0, 1, 3, 0.5, "squared", margin="bf16",
-                            take_other=np.array([True, False, False]))
-    assert list(out["v"]) == [1.0 + 2.0 ** -7, 1.0, 1.0 + 2.0 ** -6]
+    nearest, lo, hi = O.margin_choices(Y, w0)
+    assert list(nearest[:3]) == [1.0, 1.0, 1.0 + 2.0 ** -6]
+    assert list(lo[:3]) == [1.0, 1.0, 1.0 + 2.0 ** -7]
+    assert list(hi[:3]) == [1.0 + 2.0 ** -7, 1.0, 1.0 + 2.0 ** -6]
+    Y2 = np.array([[1.0, -1.0]])
+    w2 = np.array([1.0, 1.0 - 2.0 ** -20])
+    n2, lo2, hi2 = O.margin_choices(Y2, w2)
+    assert n2[0] == 2.0 ** -20
+    # e = 2 * 2^-24 / (1 - 2^-23) * (2 - 2^-20) + 2^-23 * 2^-20, about 2^-22
+    assert lo2[0] == 0.75 * 2.0 ** -20 and hi2[0] == 1.25 * 2.0 ** -20
 
 
 def _f32_dot_orders(y, w, rng):
@@ -502,10 +502,11 @@ def test_margin_choices_cover_float32_orders():
     X = (rng.standard_normal((300, n)) / np.sqrt(n)).astype(np.float32)
     Y = O.stored_values(X, "bf16")
     w0 = rng.standard_normal(n).astype(np.float32)
-    nearest, other, amb = O.margin_choices(Y, w0)
-    # the worst-case bound leaves most rows with a single admissible value
-    assert 0 < amb.sum() < 0.5 * len(amb)
+    nearest, lo, hi = O.margin_choices(Y, w0)
+    assert np.all((lo <= nearest) & (nearest <= hi))
+    # at this n the worst-case bound still leaves most rows one admissible value
+    assert 0 < np.sum(lo != hi) < 0.5 * len(lo)
     for i in range(Y.shape[0]):
         for v32 in _f32_dot_orders(Y[i], w0, rng):
             got = float(torch.tensor([float(v32)], dtype=torch.float32).to(torch.bfloat16).to(torch.float64)[0])
-            assert got == nearest[i] or (amb[i] and got == other[i]), (i, float(v32), nearest[i], other[i])
+            assert lo[i] <= got <= hi[i], (i, float(v32), lo[i], hi[i])
