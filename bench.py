@@ -228,6 +228,18 @@ def main():
         stop.record(stream)
         torch.cuda.synchronize()
         ms_plain = start.elapsed_time(stop)
+        # the recipe's bf16-stored margins: the same K steps, unstamped
+        h.set_option(B.OPT_MARGIN_BF16, 1)
+        w4 = torch.zeros(wl.n, device=dev)
+        h.train(wl.s, wl.b, wl.eta, 0, 0, args.warmup, w4)
+        torch.cuda.synchronize()
+        start.record(stream)
+        h.train(wl.s, wl.b, wl.eta, 0, args.warmup, args.steps, w4)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ms_mix = start.elapsed_time(stop)
+        loss_mix = h.loss_value(w4)
+        h.set_option(B.OPT_MARGIN_BF16, 0)
         # breakdown: the steps queued one by one as separate kernels
         for kid in B.KERNEL_NAMES:
             h.timing(kid, reset=True)
@@ -296,6 +308,8 @@ def main():
                           "frac": t_roof * 1e6 / (ms_per_step * 1e3)},
         "kernels": kernels,
         "final_loss": loss,
+        "margin_bf16": {"value": wl.s * args.steps / (ms_mix / 1e3), "unit": "inner SGD steps/s",
+                        "ms_per_step": ms_mix / args.steps, "final_loss": loss_mix},
     }
     if sgd:
         out["sgd_baseline"] = {"kind": "minibatch SGD, s = 1, same library and b, eta", **sgd}
