@@ -66,6 +66,43 @@ __device__ __forceinline__ float take(const unsigned long long* p, uint32_t epoc
   }
 }
 
+// Spin until every word p[lane + 64 u] with lane + 64 u < cnt (u < N)
+// carries `epoch`; out[u] gets its float (0 for words past cnt).  The N words
+// of a lane are polled together, so a lane that holds several columns waits
+// one round trip per poll, not one per column.  Bounded like take(): on
+// expiry sets *abort and bit 0 of *status, and the missing words read 0.
+template <int N>
+__device__ __forceinline__ void take_n(const unsigned long long* p, int lane, int cnt, uint32_t epoch,
+                                       float (&out)[N], int* status, int* abort_flag, long limit) {
+  uint32_t need = 0;
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    out[u] = 0.f;
+    if (lane + 64 * u < cnt) need |= 1u << u;
+  }
+  long it = 0;
+  while (need) {
+    uint64_t x[N];
+    // every load unconditional (words past cnt read word 0), then all checked
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int k = lane + 64 * u;
+      x[u] = __hip_atomic_load(&p[k < cnt ? k : 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+      if (((need >> u) & 1u) && static_cast<uint32_t>(x[u] >> 32) == epoch) {
+        out[u] = __uint_as_float(static_cast<uint32_t>(x[u]));
+        need &= ~(1u << u);
+      }
+    if (need && ++it > limit) {
+      *abort_flag = 1;
+      atomicOr(status, 1);
+      break;
+    }
+  }
+}
+
 // A margin as the recurrence stores it: float32, or (vround) rounded to the
 // nearest bf16, ties to even, and held in a float.
 __device__ __forceinline__ float stored_margin(float v, int vround) {

@@ -242,13 +242,11 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
         }
       }
       if (j > 0) {
+        chain::take_n<CP>(&mbox[jb - b], lane, b, a.epoch, rp, a.status, &abort_flag, a.spin);
 #pragma unroll
         for (int u = 0; u < CP; ++u) {
           const int l = lane + 64 * u;
-          if (l < b) {
-            rp[u] = chain::take(&mbox[jb - b + l], a.epoch, a.status, &abort_flag, 0, a.spin);
-            rs[jb - b + l] = rp[u];
-          }
+          if (l < b) rs[jb - b + l] = rp[u];
         }
         lds_publish(&r_ready, j);
         if (!acc_now) {
@@ -288,7 +286,11 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
     // the last block's r, for the update
     if (!abort_flag) {
       const int jb = (s - 1) * b;
-      for (int l = lane; l < b; l += 64) rs[jb + l] = chain::take(&mbox[jb + l], a.epoch, a.status, &abort_flag, 0, a.spin);
+      float rl[CP];
+      chain::take_n<CP>(&mbox[jb], lane, b, a.epoch, rl, a.status, &abort_flag, a.spin);
+#pragma unroll
+      for (int u = 0; u < CP; ++u)
+        if (lane + 64 * u < b) rs[jb + lane + 64 * u] = rl[u];
       if (!abort_flag) lds_publish(&r_ready, s);
     }
   } else {
