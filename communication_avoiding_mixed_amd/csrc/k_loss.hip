@@ -111,6 +111,68 @@ __global__ __launch_bounds__(256) void loss_kernel(const T* __restrict__ Xs,
   if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
 }
 
+// Narrow rows (at most GS 16-byte chunks, GS = 4 or 8): a wave takes 64
+// consecutive rows per pass.  Load r (r < GS) reads rows base + r*G ... base +
+// r*G + G-1 (G = 64/GS lane groups, one row per group, lane c of a group
+// chunk c), so each load instruction covers G whole consecutive rows; the
+// group sums give every lane of group g the margins of its GS rows, and lane
+// (g, c) keeps row c's, so the float64 loss terms of the 64 rows run on all 64
+// lanes.  A row's float32 dot product is summed in the same order as in
+// loss_kernel (chunk elements in order, then the group butterfly).
+template <typename T, int LOSS, int GS>
+__global__ __launch_bounds__(256) void loss_narrow_kernel(const T* __restrict__ Xs,
+                                                          const float* __restrict__ y, int64_t m,
+                                                          int64_t n, int64_t ld,
+                                                          const float* __restrict__ w,
+                                                          double* __restrict__ partial) {
+  constexpr int E = Widen<T>::kElems;
+  constexpr int G = 64 / GS;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane % GS;  // chunk of this lane
+  const int g = lane / GS;  // lane group
+  const int64_t cpr = ld / E;
+  float wv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int64_t col = static_cast<int64_t>(c) * E + e;
+    wv[e] = (c < cpr && col < n) ? w[col] : 0.f;
+  }
+  const int cc = c < cpr ? c : 0;  // chunks past the row read chunk 0 against zero weights
+  double acc = 0.0;
+  for (int64_t base = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * 64; base < m;
+       base += static_cast<int64_t>(gridDim.x) * 256) {
+    u32x4 q[GS];
+#pragma unroll
+    for (int r = 0; r < GS; ++r) {
+      const int64_t row = base + r * G + g;
+      const int64_t rc = row < m ? row : m - 1;
+      q[r] = reinterpret_cast<const u32x4*>(Xs + rc * ld)[cc];
+    }
+    float mine = 0.f;
+#pragma unroll
+    for (int r = 0; r < GS; ++r) {
+      float f[E];
+      Widen<T>::run(q[r], f);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) d = fmaf(f[e], wv[e], d);
+      const float tot = group_sum<GS>(d);
+      if (c == r) mine = tot;
+    }
+    const int64_t myrow = base + c * G + g;
+    if (myrow < m) acc += loss_value<LOSS>(static_cast<double>(mine), static_cast<double>(y[myrow]));
+  }
+  __shared__ double red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
 __global__ __launch_bounds__(256) void loss_finish_kernel(const double* __restrict__ partial, int np,
                                                           double inv_m, double* __restrict__ out) {
   __shared__ double red[256];
@@ -134,8 +196,15 @@ void loss_g(const T* X, const float* y, int64_t m, int64_t n, int64_t ld, const 
     loss_kernel<T, LOSS, GS, false><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
 }
 
+// A narrow-kernel block takes 256 rows per pass: no more blocks than passes need.
+inline int narrow_blocks(int64_t m) {
+  const int64_t need = (m + 255) / 256;
+  return static_cast<int>(need < kLossBlocks ? need : kLossBlocks);
+}
+
+// Launches the loss kernel for this row width; returns the partial sums it writes.
 template <typename T, int LOSS>
-void loss_gs(const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld, const float* w,
+int loss_gs(const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld, const float* w,
              double* partial, hipStream_t st) {
   const int64_t cpr = ld / Widen<T>::kElems;
   const T* X = static_cast<const T*>(Xs);
@@ -145,21 +214,21 @@ void loss_gs(const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld, c
     loss_g<T, LOSS, 32>(X, y, m, n, ld, w, partial, st);
   else if (cpr >= 16)
     loss_g<T, LOSS, 16>(X, y, m, n, ld, w, partial, st);
-  else if (cpr >= 8)
+  else if (cpr > 8)
     loss_g<T, LOSS, 8>(X, y, m, n, ld, w, partial, st);
+  else if (cpr > 4)  // the narrow kernels read chunks [0, GS) only
+    loss_narrow_kernel<T, LOSS, 8><<<narrow_blocks(m), 256, 0, st>>>(X, y, m, n, ld, w, partial);
   else
-    loss_g<T, LOSS, 4>(X, y, m, n, ld, w, partial, st);
+    loss_narrow_kernel<T, LOSS, 4><<<narrow_blocks(m), 256, 0, st>>>(X, y, m, n, ld, w, partial);
+  return cpr > 8 ? kLossBlocks : narrow_blocks(m);
 }
 
 template <typename T>
-void loss_t(int loss, const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld,
-            const float* w, double* partial, hipStream_t st) {
-  if (loss == kLogistic)
-    loss_gs<T, kLogistic>(Xs, y, m, n, ld, w, partial, st);
-  else if (loss == kSquared)
-    loss_gs<T, kSquared>(Xs, y, m, n, ld, w, partial, st);
-  else
-    loss_gs<T, kPoisson>(Xs, y, m, n, ld, w, partial, st);
+int loss_t(int loss, const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld,
+           const float* w, double* partial, hipStream_t st) {
+  if (loss == kLogistic) return loss_gs<T, kLogistic>(Xs, y, m, n, ld, w, partial, st);
+  if (loss == kSquared) return loss_gs<T, kSquared>(Xs, y, m, n, ld, w, partial, st);
+  return loss_gs<T, kPoisson>(Xs, y, m, n, ld, w, partial, st);
 }
 
 }  // namespace
@@ -167,13 +236,11 @@ void loss_t(int loss, const void* Xs, const float* y, int64_t m, int64_t n, int6
 hipError_t launch_loss(int storage, int loss, const void* Xs, const float* y, int64_t m, int64_t n,
                        int64_t ld, const float* w, double* partial, double* out_dev,
                        hipStream_t st) {
-  if (storage == kStoreBF16)
-    loss_t<uint16_t>(loss, Xs, y, m, n, ld, w, partial, st);
-  else
-    loss_t<float>(loss, Xs, y, m, n, ld, w, partial, st);
+  const int np = storage == kStoreBF16 ? loss_t<uint16_t>(loss, Xs, y, m, n, ld, w, partial, st)
+                                       : loss_t<float>(loss, Xs, y, m, n, ld, w, partial, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  loss_finish_kernel<<<1, 256, 0, st>>>(partial, kLossBlocks, 1.0 / static_cast<double>(m), out_dev);
+  loss_finish_kernel<<<1, 256, 0, st>>>(partial, np, 1.0 / static_cast<double>(m), out_dev);
   return hipGetLastError();
 }
 

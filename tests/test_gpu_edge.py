@@ -256,3 +256,29 @@ def test_expired_waits_are_reported_and_cleared(rec):
     assert val == fresh.loss_value(w2)
     with pytest.raises(B.CasgdError):
         h.set_option(B.OPT_SPIN_LIMIT, -1)
+
+
+# Every loss-kernel path: rows of at most 4 and at most 8 16-byte chunks (the
+# narrow kernels), 9-15 chunks, 16 or more; both storages (bf16: 8 values per
+# chunk, float32: 4); row counts that leave a partial pass, and a single row.
+@pytest.mark.parametrize("storage", ["bf16", "fp32"])
+@pytest.mark.parametrize("loss", ["logistic", "squared", "poisson"])
+@pytest.mark.parametrize("m,n", [
+    (1, 5),         # one row
+    (1000, 1),      # ld 32: 4 chunks (bf16), 8 (float32)
+    (4099, 28),     # HIGGS width: 4 / 8 chunks
+    (777, 33),      # ld 64: 8 / 16 chunks
+    (2050, 70),     # ld 96: 12 / 24 chunks
+    (513, 130),     # ld 160: 20 / 40 chunks
+    (300, 520),     # ld 544: 68 / 136 chunks
+])
+def test_loss_every_row_width(storage, loss, m, n):
+    rng = np.random.default_rng(m * 1000 + n)
+    X = (rng.standard_normal((m, n)) / np.sqrt(n)).astype(np.float32)
+    y = _targets(loss, m, seed=n)
+    h = B.CASGD(torch_dev(X), torch_dev(y), loss, storage)
+    for w0 in (np.zeros(n, np.float32), (0.5 * rng.standard_normal(n)).astype(np.float32)):
+        got = h.loss_value(torch_dev(w0))
+        ref = O.full_loss(X, y, w0.astype(np.float64), loss, storage=storage)
+        assert abs(got - ref) <= REL_TOL * abs(ref), (storage, loss, m, n, got, ref)
+    h.close()
