@@ -307,6 +307,43 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
       }
       int k0 = tb + 2;
       k0 += (h - k0 % nf + nf) % nf;  // first k >= tb+2 with k = h (mod nf)
+      if (!a.preload) {
+        // G in global memory (rows too large for LDS): up to NBW blocks'
+        // loads are all issued (clamped, unconditional) before any is used,
+        // so a fold step waits about one memory latency, not one per pair
+        constexpr int NBW = NO * CP <= 4 ? 12 : 3;
+        for (int k = k0; k < s; k += NBW * nf) {
+          float gb[NBW][NO][CP];
+#pragma unroll
+          for (int e = 0; e < NBW; ++e) {
+            const int kk = k + e * nf;
+            const int kc = kk < s ? kk : s - 1;
+#pragma unroll
+            for (int t = 0; t < NO; ++t)
+#pragma unroll
+              for (int u = 0; u < CP; ++u) {
+                const int l = lane + 64 * u;
+                gb[e][t][u] = gval(kc, t < nown ? t : 0, tb * b + (l < b ? l : 0));
+              }
+          }
+#pragma unroll
+          for (int e = 0; e < NBW; ++e) {
+            const int kk = k + e * nf;
+#pragma unroll
+            for (int t = 0; t < NO; ++t)
+#pragma unroll
+              for (int u = 0; u < CP; ++u) {
+                const int l = lane + 64 * u;
+                if (kk < s && t < nown && l < b) {
+                  float* ap = &acc[(kk * nown_max + t) * LWc + l];
+                  *ap = fmaf(gb[e][t][u], rr[u], *ap);
+                }
+              }
+          }
+        }
+        lds_publish(&acc_ready[h], tb + 1);
+        return;
+      }
       for (int k = k0; k < s; k += 2 * nf) {
         float gb[2][NO][CP], ab[2][NO][CP];
 #pragma unroll
