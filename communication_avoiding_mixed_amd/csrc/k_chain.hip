@@ -175,7 +175,13 @@ constexpr int kUpdRows = 4;  // rows per lane per block the update wave prefetch
 // block as r arrives (the rows of the next block prefetched), reduces over
 // its lanes and writes w, and the function returns true; otherwise the
 // caller runs the update afterwards.
-template <typename T, int LOSS, int NO, int CP>
+// PRE: where the rows of G are, 1 in LDS (a.preload), 0 in global memory,
+// fixed at compile time so the critical wave's loop carries no branch on
+// it; 2 reads a.preload at run time.  Measured on MI355X, the compile-time
+// forms are 3-10% faster per step for 2 and 4 rows per workgroup and the
+// run-time form 8% faster for one row and one column per lane, so each
+// variant is launched in its faster form.
+template <typename T, int LOSS, int NO, int CP, int PRE>
 __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
   const ChainArgs& a = *x.a;
   const int s = a.s, b = a.b, Q = a.Q, sb = s * b;
@@ -190,7 +196,7 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
   const unsigned long long* mbox = x.mbox;
   auto gval = [&](int k, int t, int col) -> float {
     const int64_t tri = static_cast<int64_t>(k) * (k - 1) / 2;
-    if (a.preload) return ((const lds_f32*)x.gl)[t * x.P + static_cast<int64_t>(b) * tri + col];
+    if (PRE == 1 || (PRE == 2 && a.preload)) return ((const lds_f32*)x.gl)[t * x.P + static_cast<int64_t>(b) * tri + col];
     const int64_t i = q + static_cast<int64_t>(Q) * t;
     return ((const global_f32*)a.G)[static_cast<int64_t>(b) * b * tri + i * k * b + col];
   };
@@ -307,7 +313,7 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
       }
       int k0 = tb + 2;
       k0 += (h - k0 % nf + nf) % nf;  // first k >= tb+2 with k = h (mod nf)
-      if (!a.preload) {
+      if (PRE == 0 || (PRE == 2 && !a.preload)) {
         // G in global memory (rows too large for LDS): up to NBW blocks'
         // loads are all issued (clamped, unconditional) before any is used,
         // so a fold step waits about one memory latency, not one per pair
@@ -640,9 +646,10 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
     FastCtx x{&a, q, nown, nown_max, lane, wave, rs, vown, yown, acc, gl, P, &abort_flag, &r_ready, acc_ready, mbox};
     const int fc = fast_cols(nown_max, cpl);
     bool updated;
-    if (fc == 1) updated = recurrence_fast<T, LOSS, 1, 1>(x);
-    else if (fc == 2) updated = recurrence_fast<T, LOSS, 2, 2>(x);
-    else updated = recurrence_fast<T, LOSS, kMaxOwn, kMaxCpl>(x);
+    if (fc == 1) updated = recurrence_fast<T, LOSS, 1, 1, 2>(x);
+    else if (fc == 2) updated = a.preload ? recurrence_fast<T, LOSS, 2, 2, 1>(x) : recurrence_fast<T, LOSS, 2, 2, 0>(x);
+    else updated = a.preload ? recurrence_fast<T, LOSS, kMaxOwn, kMaxCpl, 1>(x)
+                             : recurrence_fast<T, LOSS, kMaxOwn, kMaxCpl, 0>(x);
     __syncthreads();
     if (abort_flag || updated) return;
   } else {
