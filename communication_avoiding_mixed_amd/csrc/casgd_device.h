@@ -49,17 +49,24 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 //   logistic: -y * sigmoid(-y z) (exp of a non-positive argument only)
 //   squared:  z - y
 //   poisson:  exp(z) - y
+// It sits on the recurrence's critical path once per inner step, so it uses
+// the hardware exponential (v_exp_f32 of x log2 e) and reciprocal
+// (v_rcp_f32, 1 ulp): a few float32 ulps, far below the recurrence's
+// float32 rounding of z.
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
 template <int LOSS>
 __device__ __forceinline__ float loss_deriv(float z, float y) {
   if constexpr (LOSS == kLogistic) {
     const float u = -y * z;
-    const float e = expf(-fabsf(u));
-    const float sig = u >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+    const float e = exp_hw(-fabsf(u));
+    const float inv = __builtin_amdgcn_rcpf(1.f + e);
+    const float sig = u >= 0.f ? inv : e * inv;
     return -y * sig;
   } else if constexpr (LOSS == kSquared) {
     return z - y;
   } else {
-    return expf(z) - y;
+    return exp_hw(z) - y;
   }
 }
 
