@@ -40,6 +40,9 @@ def _data(loss, m, n, seed):
     (4000, 2000, 16, 64, 3),  # the epsilon step shape
     (3000, 1800, 3, 128, 3),  # update after the recurrence (8 rows per lane per block)
     (2000, 3000, 2, 32, 3),   # ld 3008: weights read from global memory in the margins
+    (3000, 28, 32, 128, 2),   # HIGGS-like: G rows too large for LDS, 2 rows per workgroup
+    (4000, 512, 8, 256, 2),   # synth-like: 4 rows per workgroup, 4 columns per lane
+    (2000, 64, 40, 64, 2),    # one row per workgroup with G too large for LDS
 ])
 def test_train_equals_outer_steps(loss, m, n, s, b, n_outer):
     import torch
