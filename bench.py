@@ -128,6 +128,7 @@ def sgd_baselines(h_bf16, X, y, wl, steps: int, warmup: int, dev):
         h = h_bf16 if storage == "bf16" else B.CASGD(torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev),
                                                      wl.loss, "fp32")
         w = torch.zeros(wl.n, device=dev)
+        stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(stream):
             h.train(1, wl.b, wl.eta, 7, 0, warmup * wl.s, w)
             start = torch.cuda.Event(enable_timing=True)
@@ -171,6 +172,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sgd-baseline", action="store_true",
                     help="skip the plain minibatch SGD runs (s = 1) of the same library")
+    ap.add_argument("--layout", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="placement of the recurrence's workgroups (CASGD_OPT_CHAIN_LAYOUT): "
+                         "0 automatic, 1 spread over the XCDs, 2 on one XCD, one per CU, "
+                         "3 on one XCD, up to two per CU")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES between two device buffers (a plain copy kernel of "
                          "known traffic, to scale the HBM byte counters) and exit")
@@ -196,8 +201,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     h = B.CASGD(torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev), wl.loss, wl.storage)
+    h.set_option(B.OPT_CHAIN_LAYOUT, args.layout)
     stream = torch.cuda.Stream()
     w = torch.zeros(wl.n, device=dev)
+    # the zero fill above runs on the default stream; the timed stream waits for it
+    stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
         # warm-up
         h.train(wl.s, wl.b, wl.eta, 0, 0, args.warmup, w)

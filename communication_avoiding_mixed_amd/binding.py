@@ -20,10 +20,12 @@ LOGISTIC, SQUARED, POISSON = 0, 1, 2
 BF16, FP32 = 0, 1
 OK, EINVAL, ENOMEM, EHIP = 0, -1, -2, -3
 EXPORT_IDX, EXPORT_Y, EXPORT_YB, EXPORT_G, EXPORT_V, EXPORT_Z, EXPORT_R = range(7)
-K_GATHER, K_GRAM, K_CHAIN, K_PIPE = range(4)
-OPT_RECURRENCE, OPT_SPIN_LIMIT, OPT_MARGIN_BF16 = 0, 1, 2
+K_GATHER, K_GRAM, K_CHAIN, K_PIPE, K_TRAIN = range(5)
+OPT_RECURRENCE, OPT_SPIN_LIMIT, OPT_MARGIN_BF16, OPT_CHAIN_LAYOUT, OPT_TRAIN_FORM = 0, 1, 2, 3, 4
+TRAIN_PERSISTENT, TRAIN_PER_STEP = 0, 1
+LAYOUT_AUTO, LAYOUT_SPREAD, LAYOUT_ONE_XCD = 0, 1, 2
 RECURRENCE_AUTO, RECURRENCE_ALL_TO_ALL, RECURRENCE_LOOKAHEAD = 0, 1, 2
-KERNEL_NAMES = {K_GATHER: "gather", K_GRAM: "gram", K_CHAIN: "chain", K_PIPE: "pipe"}
+KERNEL_NAMES = {K_GATHER: "gather", K_GRAM: "gram", K_CHAIN: "chain", K_PIPE: "pipe", K_TRAIN: "train"}
 
 LOSS_IDS = {"logistic": LOGISTIC, "squared": SQUARED, "poisson": POISSON}
 STORAGE_IDS = {"bf16": BF16, "fp32": FP32}

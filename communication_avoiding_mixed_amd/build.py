@@ -21,7 +21,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcasgd.so")
 
-SOURCES = ["casgd_api.hip", "k_gather.hip", "k_gram.hip", "k_chain.hip", "k_chain_la.hip", "k_loss.hip"]
+SOURCES = ["casgd_api.hip", "k_gather.hip", "k_gram.hip", "k_chain.hip", "k_chain_la.hip", "k_loss.hip",
+           "k_step.hip", "k_step_1x1.hip", "k_step_2x1.hip", "k_step_2x2.hip", "k_step_4x2.hip",
+           "k_step_4x4.hip"]
 HEADERS = ["casgd_device.h", "casgd_internal.h", "casgd_chain.h"]
 
 ARCH = "gfx950"
@@ -55,7 +57,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     jobs = []
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 8, 16)) as ex:
         for src in SOURCES:
             obj = os.path.join(BUILD, src.replace(".hip", ".o"))
             objs.append(obj)

@@ -22,6 +22,7 @@
 #include "casgd_gather.h"
 #include "casgd_chain.h"
 #include "casgd_internal.h"
+#include "casgd_train.h"
 
 namespace {
 
@@ -39,6 +40,9 @@ int hip_fail(hipError_t e, const char* what) {
 constexpr int kMaxSB = 16384;
 constexpr int kPipeGatherWgs = 64;  // gather workgroups of a pipelined step launch
 constexpr int kMarginRows = 8;      // rows per margin workgroup of a pipelined step launch
+// progress words of the persistent launch: gfree[64] | wdone[64] | gprog[up to kMaxGramWgs]
+constexpr int kMaxGramWgs = 1024;
+constexpr int kProgWords = 128 + kMaxGramWgs;
 
 struct EventPair {
   hipEvent_t start = nullptr;
@@ -64,6 +68,8 @@ struct casgd_ctx {
   hipStream_t prep = nullptr;    // internal: sampling, gather, Gram
   hipEvent_t ev_prep[2] = {nullptr, nullptr};
   hipEvent_t ev_chain[2] = {nullptr, nullptr};
+  hipEvent_t ev_switch = nullptr;  // orders a new caller stream after the old one
+  int xcds = 1, cus = 1;           // XCDs and CUs of the device
 
   // workspace, sized for cap_sb rows and cap_g Gram elements
   int cap_sb = 0;
@@ -74,8 +80,12 @@ struct casgd_ctx {
   float* r = nullptr;
   int32_t* idx_user = nullptr;
   unsigned long long* xbuf = nullptr;
-  int* order = nullptr;          // Gram workgroup -> tile table for (order_s, order_b)
-  int order_cap = 0, order_s = 0, order_b = 0;
+  // Gram workgroup -> tile tables for (order_s, order_b): [0] for tiles over
+  // all XCDs (stand-alone Gram), [1] over the XCDs left to the other roles of
+  // a pipelined step launch whose recurrence sits on one XCD
+  int* order[2] = {nullptr, nullptr};
+  int order_cap[2] = {0, 0}, order_s[2] = {0, 0}, order_b[2] = {0, 0}, order_nx[2] = {0, 0};
+  unsigned long long* place = nullptr;  // XCD of each chain workgroup (tagged words)
   int* status = nullptr;
   double* loss_partial = nullptr;
   double* loss_out = nullptr;
@@ -83,6 +93,10 @@ struct casgd_ctx {
   int recurrence = 0;  // CASGD_OPT_RECURRENCE
   long spin = 0;       // CASGD_OPT_SPIN_LIMIT (0: the default bound)
   int margin_bf16 = 0; // CASGD_OPT_MARGIN_BF16
+  int layout = 0;      // CASGD_OPT_CHAIN_LAYOUT
+  int train_form = 0;  // CASGD_OPT_TRAIN_FORM
+  unsigned long long* prog = nullptr;  // progress words of the persistent launch
+  unsigned long long* wbox = nullptr;  // tagged weights of the persistent launch (n words)
 
   int next_buf = 0;
   int last_buf = 0;
@@ -116,8 +130,10 @@ void free_workspace(casgd_ctx* h) {
   release(h->r);
   release(h->idx_user);
   release(h->xbuf);
-  release(h->order);
-  h->order_cap = h->order_s = h->order_b = 0;
+  for (int i = 0; i < 2; ++i) {
+    release(h->order[i]);
+    h->order_cap[i] = h->order_s[i] = h->order_b[i] = h->order_nx[i] = 0;
+  }
   h->cap_sb = 0;
   h->cap_g = 0;
 }
@@ -168,26 +184,41 @@ int ensure_workspace(casgd_ctx* h, int s, int b) {
   return CASGD_OK;
 }
 
-// The Gram's XCD-grouped tile order for shape (s, b), rebuilt when the shape changes.
-int ensure_order(casgd_ctx* h, int s, int b) {
-  if (h->order && h->order_s == s && h->order_b == b) return CASGD_OK;
-  const std::vector<int> order = casgd::gram_order(s, b);
+// The Gram's XCD-grouped tile order for shape (s, b) over nx XCDs in table
+// `which`, rebuilt when the shape changes.
+int ensure_order(casgd_ctx* h, int which, int s, int b, int nx) {
+  if (h->order[which] && h->order_s[which] == s && h->order_b[which] == b && h->order_nx[which] == nx)
+    return CASGD_OK;
+  const std::vector<int> order = casgd::gram_order(s, b, nx);
   hipError_t e = sync_all(h);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-  if (static_cast<int>(order.size()) > h->order_cap) {
-    release(h->order);
-    h->order_cap = 0;
-    if (!grab(h->order, sizeof(int) * (order.size() > 0 ? order.size() : 1)))
+  if (static_cast<int>(order.size()) > h->order_cap[which]) {
+    release(h->order[which]);
+    h->order_cap[which] = 0;
+    if (!grab(h->order[which], sizeof(int) * (order.size() > 0 ? order.size() : 1)))
       return fail(CASGD_ENOMEM, "device allocation of the Gram tile order failed");
-    h->order_cap = static_cast<int>(order.size());
+    h->order_cap[which] = static_cast<int>(order.size());
   }
   if (!order.empty()) {
-    e = hipMemcpy(h->order, order.data(), sizeof(int) * order.size(), hipMemcpyHostToDevice);
+    e = hipMemcpy(h->order[which], order.data(), sizeof(int) * order.size(), hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "uploading the Gram tile order");
   }
-  h->order_s = s;
-  h->order_b = b;
+  h->order_s[which] = s;
+  h->order_b[which] = b;
+  h->order_nx[which] = nx;
   return CASGD_OK;
+}
+
+// Layout of the recurrence's workgroups for (s, b) on this handle.
+casgd::ChainPlan plan_chain(const casgd_ctx* h, int s, int b) {
+  return casgd::chain_plan(s, b, h->ld, h->xcds, h->cus / h->xcds, h->layout);
+}
+
+int launch_fail(hipError_t e, const char* what) {
+  if (e == hipErrorLaunchOutOfResources)
+    return fail(CASGD_EHIP, std::string(what) +
+                                ": the recurrence's workgroups cannot all be resident at once on this device");
+  return hip_fail(e, what);
 }
 
 EventPair take_pair(casgd_ctx* h) {
@@ -238,7 +269,7 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
               float* w) {
   int rc = ensure_workspace(h, s, b);
   if (rc != CASGD_OK) return rc;
-  rc = ensure_order(h, s, b);
+  rc = ensure_order(h, 0, s, b, casgd::kXcds);
   if (rc != CASGD_OK) return rc;
   const int sb = s * b;
   const float c = eta / static_cast<float>(b);
@@ -256,7 +287,7 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   if (e != hipSuccess) return hip_fail(e, "gather launch");
   const casgd::GramPlan plan = casgd::gram_plan(h->storage, s, b, h->ld);
   e = timed(h, CASGD_K_GRAM, [&](const casgd::LaunchTimer& tm) {
-    return casgd::launch_gram(h->storage, B.Y, h->ld, s, b, B.G, plan, h->order, h->prep, tm);
+    return casgd::launch_gram(h->storage, B.Y, h->ld, s, b, B.G, plan, h->order[0], h->prep, tm);
   });
   if (e != hipSuccess) return hip_fail(e, "gram launch");
   e = hipEventRecord(h->ev_prep[k], h->prep);
@@ -271,7 +302,11 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   a.n = h->n;
   a.s = s;
   a.b = b;
-  a.Q = casgd::chain_workgroups(s, b);
+  const casgd::ChainPlan cp = plan_chain(h, s, b);
+  a.Q = cp.Q;
+  a.stride = cp.stride;
+  a.place = (cp.stride > 1 || h->xcds == 1) ? h->place : nullptr;
+  a.cus = h->cus;
   a.c = c;
   a.G = B.G;
   a.yB = B.yB;
@@ -287,17 +322,152 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   // The all-to-all kernel is the faster one on every measured shape, so it is
   // the default; the lookahead form runs only when asked for.
   const casgd::LaPlan la = h->recurrence == 2 ? casgd::la_plan(s, b) : casgd::LaPlan{};
-  if (la.ok) a.Q = casgd::kChainMaxWorkgroups;
-  e = timed(h, CASGD_K_CHAIN, [&](const casgd::LaunchTimer& tm) {
-    return la.ok ? casgd::launch_chain_la(h->storage, h->loss, a, la, h->stream, tm)
-                 : casgd::launch_chain(h->storage, h->loss, a, h->stream, tm);
-  });
-  if (e != hipSuccess) return hip_fail(e, "recurrence launch");
+  if (la.ok) {
+    a.Q = casgd::kChainMaxWorkgroups;
+    a.stride = 1;
+    a.place = nullptr;
+  }
+  if (!la.ok && cp.lean) {
+    // the lean recurrence with its margins computed by workgroups of the same
+    // launch (the launch casgd_train uses, without the Gram and gather roles)
+    casgd::PipeArgs p;
+    p.a = a;
+    p.a.preload = 0;
+    p.vbox_out = h->xbuf + static_cast<int64_t>(casgd::kChainMaxWorkgroups) * sb;
+    p.a.vbox = p.vbox_out;
+    p.ochain = (a.Q + casgd::kXcds - 1) / casgd::kXcds * casgd::kXcds;
+    p.mar0 = 0;
+    p.mar_rows = kMarginRows;
+    p.mar_wgs = (sb + kMarginRows - 1) / kMarginRows;
+    e = timed(h, CASGD_K_CHAIN, [&](const casgd::LaunchTimer& tm) {
+      return casgd::launch_step(h->storage, h->loss, p, h->stream, tm);
+    });
+  } else {
+    e = timed(h, CASGD_K_CHAIN, [&](const casgd::LaunchTimer& tm) {
+      return la.ok ? casgd::launch_chain_la(h->storage, h->loss, a, la, h->stream, tm)
+                   : casgd::launch_chain(h->storage, h->loss, a, h->stream, tm);
+    });
+  }
+  if (e != hipSuccess) return launch_fail(e, "recurrence launch");
   e = hipEventRecord(h->ev_chain[k], h->stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   h->last_buf = k;
   h->next_buf = k ^ 1;
+  h->last_s = s;
+  h->last_b = b;
+  return CASGD_OK;
+}
+
+// Rows per margin workgroup of the persistent launch for (s, b): about half
+// of the workgroups besides the recurrence's compute margins (few rows each,
+// so a step's margins come out soon after its weights), at least
+// kMarginRows rows each, fewer when their rows (staged in LDS) would not
+// fit; 0 if no choice fits, or the margins would need more than half of
+// those workgroups.
+int persist_margin_rows(const casgd_ctx* h, const casgd::ChainPlan& cp, int s, int b) {
+  const int cus_per_xcd = h->cus / h->xcds;
+  const int others = cp.stride > 1 ? (cp.stride - 1) * cus_per_xcd : h->cus - cp.Q;
+  const int sb = s * b;
+  if (others < 16) return 0;
+  int rows = (sb + others / 2 - 1) / (others / 2);
+  if (rows < kMarginRows) rows = kMarginRows;
+  while (rows > 1 && casgd::train_lds(h->storage, s, b, cp.Q, h->ld, rows, false) == 0) --rows;
+  if (casgd::train_lds(h->storage, s, b, cp.Q, h->ld, rows, false) == 0) return 0;
+  return (sb + rows - 1) / rows <= others / 2 ? rows : 0;
+}
+
+// casgd_train as one persistent launch (casgd_train.h): the recurrence's
+// workgroups, margin workgroups and Gram workgroups stay resident for all n
+// steps; G of step i lives in buffer set i mod 3.  A gather of the last
+// step's rows follows, for the exports.
+int run_train_persist(casgd_ctx* h, const casgd::ChainPlan& cp, int s, int b, float eta, uint64_t base_seed,
+                      uint64_t first, int n, float* w) {
+  int rc = ensure_workspace(h, s, b);
+  if (rc != CASGD_OK) return rc;
+  const int nx = cp.stride > 1 ? cp.stride - 1 : casgd::kXcds;
+  rc = ensure_order(h, 1, s, b, nx);
+  if (rc != CASGD_OK) return rc;
+  const int sb = s * b;
+  const casgd::GramPlan gp = casgd::gram_plan(h->storage, s, b, h->ld, nx);
+  auto round_up = [](int x, int k) { return (x + k - 1) / k * k; };
+  // workgroups besides the recurrence's: everything the device holds at once
+  const int cus_per_xcd = h->cus / h->xcds;
+  const int grid = cp.stride > 1 ? cp.stride * cus_per_xcd : h->cus;
+  const int others = cp.stride > 1 ? (cp.stride - 1) * cus_per_xcd : h->cus - cp.Q;
+  const int mar_rows = persist_margin_rows(h, cp, s, b);
+  if (mar_rows <= 0) return fail(CASGD_EHIP, "persistent train launch: no layout of the margin workgroups fits");
+  const int mar_wgs = (sb + mar_rows - 1) / mar_rows;
+  // a second G buffer when it fits: G_{k+1} then arrives during step k
+  const bool dbl = casgd::train_lds(h->storage, s, b, cp.Q, h->ld, mar_rows, true) != 0;
+  // the Gram's workgroups start at a multiple of nx (counted in launch
+  // indices when the recurrence is spread) and come in multiples of nx
+  int gram0 = round_up(mar_wgs, nx);
+  if (cp.stride == 1) gram0 = round_up(cp.Q + mar_wgs, nx) - cp.Q;
+  int gram_wgs = (others - gram0) / nx * nx;
+  if (gram_wgs > kMaxGramWgs) gram_wgs = kMaxGramWgs / nx * nx;
+  if (s == 1) gram_wgs = 0;
+  if (gram_wgs <= 0 && s > 1) return fail(CASGD_EHIP, "persistent train launch: no workgroups left for the Gram");
+  casgd::persist::TrainArgs A{};
+  A.Xs = h->Xs;
+  A.y = h->y;
+  A.m = h->m;
+  A.n = h->n;
+  A.ld = h->ld;
+  A.s = s;
+  A.b = b;
+  A.Q = cp.Q;
+  A.stride = cp.stride;
+  A.loss = h->loss;
+  A.vround = h->margin_bf16;
+  A.c = eta / static_cast<float>(b);
+  A.n_outer = n;
+  A.base_seed = base_seed;
+  A.first = first;
+  A.w = w;
+  A.v = h->v;
+  A.z = h->z;
+  A.r = h->r;
+  for (int i = 0; i < casgd::persist::kRing; ++i) A.G[i] = h->buf[i].G;
+  A.xbuf = h->xbuf;
+  A.vbox = h->xbuf + static_cast<int64_t>(casgd::kChainMaxWorkgroups) * sb;
+  A.wbox = h->wbox;
+  A.place = (cp.stride > 1 || h->xcds == 1) ? h->place : nullptr;
+  A.prog = h->prog;
+  // tags of steps 0 .. n-1 (never 0: the buffers start zeroed)
+  if (h->epoch + static_cast<uint32_t>(n) + 1 < h->epoch) h->epoch = 0;
+  A.tag0 = h->epoch + 1;
+  h->epoch += static_cast<uint32_t>(n);
+  A.status = h->status;
+  A.spin = h->spin > 0 ? h->spin : casgd::chain::kSpinLimit;
+  A.ochain = cp.Q;
+  A.mar_wgs = mar_wgs;
+  A.mar_rows = mar_rows;
+  A.gram0 = gram0;
+  A.gram_wgs = gram_wgs;
+  A.tiles = gp.tiles;
+  A.tps = (b + 63) / 64;
+  A.slots = gp.slots;
+  A.order = h->order[1];
+  A.dbl = dbl ? 1 : 0;
+  A.cus = h->cus;
+  // work queued earlier on the prep stream uses the buffer sets
+  hipError_t e = hipEventRecord(h->ev_prep[0], h->prep);
+  if (e == hipSuccess) e = hipStreamWaitEvent(h->stream, h->ev_prep[0], 0);
+  if (e != hipSuccess) return hip_fail(e, "ordering the prep stream before the training launch");
+  e = timed(h, CASGD_K_TRAIN, [&](const casgd::LaunchTimer& tm) {
+    return casgd::launch_train(h->storage, A, grid, h->stream, tm);
+  });
+  if (e != hipSuccess) return launch_fail(e, "persistent training launch");
+  StepBuffers& B = h->buf[(n - 1) % 3];
+  e = casgd::launch_gather(h->storage, h->Xs, h->y, h->m, h->ld, sb,
+                           casgd::splitmix64(base_seed, first + static_cast<uint64_t>(n - 1)), nullptr, B.idx, B.Y,
+                           B.yB, h->stream);
+  if (e != hipSuccess) return hip_fail(e, "gather of the last step");
+  e = hipEventRecord(h->ev_chain[0], h->stream);
+  if (e == hipSuccess) e = hipEventRecord(h->ev_chain[1], h->stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  h->last_buf = (n - 1) % 3;
   h->last_s = s;
   h->last_b = b;
   return CASGD_OK;
@@ -312,7 +482,13 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
                    int n, float* w) {
   int rc = ensure_workspace(h, s, b);
   if (rc != CASGD_OK) return rc;
-  rc = ensure_order(h, s, b);
+  rc = ensure_order(h, 0, s, b, casgd::kXcds);
+  if (rc != CASGD_OK) return rc;
+  // recurrence on one XCD: the other roles cycle over the remaining ones
+  const casgd::ChainPlan cp = plan_chain(h, s, b);
+  const int nx = cp.stride > 1 ? cp.stride - 1 : casgd::kXcds;
+  const int ot = cp.stride > 1 ? 1 : 0;  // tile-order table of the step launch
+  rc = ensure_order(h, ot, s, b, nx);
   if (rc != CASGD_OK) return rc;
   const int sb = s * b;
   const float c = eta / static_cast<float>(b);
@@ -332,21 +508,23 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
     });
   };
   const casgd::GramPlan plan = casgd::gram_plan(h->storage, s, b, h->ld);
+  const casgd::GramPlan pplan = casgd::gram_plan(h->storage, s, b, h->ld, nx);
   e = gather(0);
   if (e == hipSuccess)
     e = timed(h, CASGD_K_GRAM, [&](const casgd::LaunchTimer& tm) {
-      return casgd::launch_gram(h->storage, h->buf[0].Y, h->ld, s, b, h->buf[0].G, plan, h->order,
+      return casgd::launch_gram(h->storage, h->buf[0].Y, h->ld, s, b, h->buf[0].G, plan, h->order[0],
                                 h->stream, tm);
     });
   if (e == hipSuccess && n > 1) e = gather(1);
   if (e != hipSuccess) return hip_fail(e, "pipeline prologue");
 
-  const int Q = casgd::chain_workgroups(s, b);
+  const int Q = cp.Q;
   const bool fast = casgd::chain_fast(s, b, Q, h->ld);
   const int64_t cpr = h->ld / (h->storage == CASGD_BF16 ? 8 : 4);  // 16-byte chunks per row
   const int gs = casgd::gather::group_size(cpr);
   const int rows_per_wg = 256 / gs;
   const int gather_wgs_all = (sb + rows_per_wg - 1) / rows_per_wg;
+  auto round_up = [](int x, int k) { return (x + k - 1) / k * k; };
   for (int i = 0; i < n; ++i) {
     StepBuffers& C = h->buf[i % 3];
     casgd::PipeArgs p;
@@ -357,6 +535,9 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
     a.s = s;
     a.b = b;
     a.Q = Q;
+    a.stride = cp.stride;
+    a.place = (cp.stride > 1 || h->xcds == 1) ? h->place : nullptr;
+    a.cus = h->cus;
     a.c = c;
     a.G = C.G;
     a.yB = C.yB;
@@ -370,25 +551,29 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
     a.spin = h->spin > 0 ? h->spin : casgd::chain::kSpinLimit;
     a.vround = h->margin_bf16;
     a.preload = 0;
-    // margins by their own workgroups (kMarginRows rows each) when the chain
-    // takes them from the exchange buffer's last s*b words
-    int next = (Q + casgd::kXcds - 1) / casgd::kXcds * casgd::kXcds;
-    if (fast) {
+    // The other roles are numbered from 0 over the non-chain workgroups
+    // (PipeArgs); the Gram's range starts at a multiple of nx so its tile
+    // order's XCD grouping holds.  Margins by their own workgroups
+    // (kMarginRows rows each) when the chain takes them from the exchange
+    // buffer's last s*b words.
+    p.ochain = round_up(Q, casgd::kXcds);
+    int next = 0;
+    if (fast || cp.lean) {
       p.vbox_out = h->xbuf + static_cast<int64_t>(casgd::kChainMaxWorkgroups) * sb;
       a.vbox = p.vbox_out;
-      p.mar0 = next;
+      p.mar0 = 0;
       p.mar_rows = kMarginRows;
       p.mar_wgs = (sb + kMarginRows - 1) / kMarginRows;
-      next = (p.mar0 + p.mar_wgs + casgd::kXcds - 1) / casgd::kXcds * casgd::kXcds;
+      next = round_up(p.mar_wgs, nx);
     }
     p.gram0 = next;
-    if (i + 1 < n && plan.tiles > 0) {
+    if (i + 1 < n && pplan.tiles > 0) {
       const StepBuffers& N = h->buf[(i + 1) % 3];
-      p.gram_slots = plan.slots;
+      p.gram_slots = pplan.slots;
       p.tps = (b + 63) / 64;
       p.gY = N.Y;
       p.gG = N.G;
-      p.order = h->order;
+      p.order = h->order[ot];
     }
     p.gath0 = p.gram0 + p.gram_slots;
     if (i + 2 < n) {
@@ -406,9 +591,10 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
       p.yBo = A.yB;
     }
     e = timed(h, CASGD_K_PIPE, [&](const casgd::LaunchTimer& tm) {
-      return casgd::launch_pipe(h->storage, h->loss, p, h->stream, tm);
+      return cp.lean ? casgd::launch_step(h->storage, h->loss, p, h->stream, tm)
+                     : casgd::launch_pipe(h->storage, h->loss, p, h->stream, tm);
     });
-    if (e != hipSuccess) return hip_fail(e, "pipelined step launch");
+    if (e != hipSuccess) return launch_fail(e, "pipelined step launch");
   }
   // later outer steps' prep work reuses sets 0 and 1 only after this loop
   e = hipEventRecord(h->ev_chain[0], h->stream);
@@ -460,10 +646,21 @@ casgd_handle casgd_create(const float* X, const float* y, int64_t m, int64_t n, 
   h->loss = loss;
   h->storage = storage;
   h->esize = storage == CASGD_BF16 ? 2 : 4;
-  bool ok = hipStreamCreateWithFlags(&h->prep, hipStreamNonBlocking) == hipSuccess;
+  bool ok = hipStreamCreateWithFlags(&h->prep, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&h->ev_switch, hipEventDisableTiming) == hipSuccess;
   for (int i = 0; i < 2 && ok; ++i)
     ok = hipEventCreateWithFlags(&h->ev_prep[i], hipEventDisableTiming) == hipSuccess &&
          hipEventCreateWithFlags(&h->ev_chain[i], hipEventDisableTiming) == hipSuccess;
+  // where the recurrence's workgroups can be placed
+  int dev = 0, xcds = 1, cus = 1;
+  ok = ok && hipGetDevice(&dev) == hipSuccess &&
+       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+  if (ok && hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    xcds = 1;
+  }
+  h->xcds = xcds >= 1 && cus % xcds == 0 ? xcds : 1;
+  h->cus = cus >= 1 ? cus : 1;
   if (!ok) {
     (void)hipGetLastError();
     fail(CASGD_EHIP, "creating the handle's stream and events failed");
@@ -472,13 +669,19 @@ casgd_handle casgd_create(const float* X, const float* y, int64_t m, int64_t n, 
   }
   if (!grab(h->Xs, h->esize * h->ld * m) || !grab(h->y, sizeof(float) * m) ||
       !grab(h->loss_partial, sizeof(double) * casgd::kLossBlocks) ||
-      !grab(h->loss_out, sizeof(double)) || !grab(h->status, sizeof(int))) {
+      !grab(h->loss_out, sizeof(double)) || !grab(h->status, sizeof(int)) ||
+      !grab(h->place, sizeof(unsigned long long) * casgd::kChainMaxWorkgroups) ||
+      !grab(h->prog, sizeof(unsigned long long) * kProgWords) || !grab(h->wbox, sizeof(unsigned long long) * n)) {
     (void)hipGetLastError();
     fail(CASGD_ENOMEM, "device allocation of the stored data failed");
     casgd_destroy(h);
     return nullptr;
   }
   hipError_t e = hipMemsetAsync(h->status, 0, sizeof(int), h->stream);
+  if (e == hipSuccess)
+    e = hipMemsetAsync(h->place, 0, sizeof(unsigned long long) * casgd::kChainMaxWorkgroups, h->stream);
+  if (e == hipSuccess) e = hipMemsetAsync(h->prog, 0, sizeof(unsigned long long) * kProgWords, h->stream);
+  if (e == hipSuccess) e = hipMemsetAsync(h->wbox, 0, sizeof(unsigned long long) * n, h->stream);
   if (e == hipSuccess) e = casgd::launch_store(storage, X, h->Xs, m, n, h->ld, h->stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(h->y, y, sizeof(float) * m, hipMemcpyDeviceToDevice, h->stream);
@@ -501,6 +704,9 @@ void casgd_destroy(casgd_handle h) {
   release(h->loss_partial);
   release(h->loss_out);
   release(h->status);
+  release(h->place);
+  release(h->prog);
+  release(h->wbox);
   for (auto& v : h->pending)
     for (auto& p : v) h->pool.push_back(p);
   for (auto& p : h->pool) {
@@ -511,13 +717,21 @@ void casgd_destroy(casgd_handle h) {
     if (h->ev_prep[i]) (void)hipEventDestroy(h->ev_prep[i]);
     if (h->ev_chain[i]) (void)hipEventDestroy(h->ev_chain[i]);
   }
+  if (h->ev_switch) (void)hipEventDestroy(h->ev_switch);
   if (h->prep) (void)hipStreamDestroy(h->prep);
   delete h;
 }
 
 int casgd_set_stream(casgd_handle h, void* stream) {
   if (!h) return fail(CASGD_EINVAL, "NULL handle");
-  h->stream = static_cast<hipStream_t>(stream);
+  hipStream_t next = static_cast<hipStream_t>(stream);
+  if (next == h->stream) return CASGD_OK;
+  // The handle's buffers are shared by all its work: the new stream starts
+  // only after everything already queued on the old one.
+  hipError_t e = hipEventRecord(h->ev_switch, h->stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(next, h->ev_switch, 0);
+  if (e != hipSuccess) return hip_fail(e, "ordering the new stream after the old one");
+  h->stream = next;
   return CASGD_OK;
 }
 
@@ -535,6 +749,14 @@ int casgd_set_option(casgd_handle h, int option, int value) {
   }
   if (option == CASGD_OPT_MARGIN_BF16 && (value == 0 || value == 1)) {
     h->margin_bf16 = value;
+    return CASGD_OK;
+  }
+  if (option == CASGD_OPT_CHAIN_LAYOUT && value >= 0 && value <= 3) {
+    h->layout = value;
+    return CASGD_OK;
+  }
+  if (option == CASGD_OPT_TRAIN_FORM && (value == 0 || value == 1)) {
+    h->train_form = value;
     return CASGD_OK;
   }
   return fail(CASGD_EINVAL, "unknown option or value");
@@ -574,8 +796,12 @@ int casgd_train(casgd_handle h, int s, int b, float eta, uint64_t base_seed, uin
   int rc = check_step_args(h, s, b, w);
   if (rc != CASGD_OK) return rc;
   if (n_outer < 0) return fail(CASGD_EINVAL, "n_outer must be >= 0");
-  if (n_outer > 0 && h->recurrence != 2)
+  if (n_outer > 0 && h->recurrence != 2) {
+    const casgd::ChainPlan cp = plan_chain(h, s, b);
+    if (cp.lean && h->train_form == 0 && persist_margin_rows(h, cp, s, b) > 0)
+      return run_train_persist(h, cp, s, b, eta, base_seed, first_step, n_outer, w);
     return run_train_pipe(h, s, b, eta, base_seed, first_step, n_outer, w);
+  }
   for (int k = 0; k < n_outer; ++k) {
     rc = run_outer(h, s, b, eta, casgd::splitmix64(base_seed, first_step + k), nullptr, w);
     if (rc != CASGD_OK) return rc;

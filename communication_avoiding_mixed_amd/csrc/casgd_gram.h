@@ -36,9 +36,25 @@ constexpr int lds_elems() {
 // is not touched until the LDS copy, so the compiler waits for exactly the
 // stage it needs and D stages stay in flight.  The stage count is padded to a
 // multiple of D with zero stages.  `lds` holds lds_elems<BK>() elements.
-template <int BK, int D>
+// Row r of the step's Y is row row_of(r) of `Y` (the gathered rows
+// themselves, or the stored data read through the sampled indices).  WT
+// writes G through to memory (device-scope stores), for readers on other
+// XCDs inside the same launch.
+struct SameRow {
+  __device__ int64_t operator()(int r) const { return r; }
+};
+
+template <bool WT>
+__device__ __forceinline__ void store_g(float* p, float v) {
+  if constexpr (WT)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
+template <int BK, int D, bool WT = false, typename RowOf = SameRow>
 __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ Y, int64_t ld, int b, int tps,
-                                          float* __restrict__ G, int tile, uint16_t* lds) {
+                                          float* __restrict__ G, int tile, uint16_t* lds, RowOf row_of = {}) {
   constexpr int CPR = BK / 8;          // 16-byte chunks per tile row per stage
   constexpr int RPP = 256 / CPR;       // tile rows loaded per pass
   constexpr int PASSES = kTile / RPP;  // passes per operand per stage
@@ -71,8 +87,8 @@ __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ Y, int64_
     const int r = lrow + q * RPP;
     const int ar = a0 + r < b ? r : 0;
     const int br = b0 + r < b ? r : 0;
-    aptr[q] = Y + (static_cast<int64_t>(j) * b + a0 + ar) * ld + lchunk * 8;
-    bptr[q] = Y + (static_cast<int64_t>(t) * b + b0 + br) * ld + lchunk * 8;
+    aptr[q] = Y + row_of(j * b + a0 + ar) * ld + lchunk * 8;
+    bptr[q] = Y + row_of(t * b + b0 + br) * ld + lchunk * 8;
   }
 
   // Chunks past the end of the row (a half-width last stage, or the zero
@@ -146,7 +162,7 @@ __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ Y, int64_
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int row = a0 + wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (row < b) gcol[row * ldg] = acc[0][e];
+      if (row < b) store_g<WT>(&gcol[row * ldg], acc[0][e]);
     }
   }
 }
@@ -157,8 +173,9 @@ __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ Y, int64_
 constexpr int kF32BK = 16;
 constexpr int kF32LdsElems = 2 * kF32BK * (kTile + 4);
 
+template <bool WT = false, typename RowOf = SameRow>
 __device__ __forceinline__ void f32_tile(const float* __restrict__ Y, int64_t ld, int b, int tps,
-                                         float* __restrict__ G, int tile, float* lds) {
+                                         float* __restrict__ G, int tile, float* lds, RowOf row_of = {}) {
   constexpr int BK = kF32BK;
   constexpr int LW = kTile + 4;
   float* As = lds;            // [BK][LW]
@@ -178,8 +195,8 @@ __device__ __forceinline__ void f32_tile(const float* __restrict__ Y, int64_t ld
   const int lr = threadIdx.x >> 2;
   const int lk = (threadIdx.x & 3) * 4;
   const bool aok = a0 + lr < b, bok = b0 + lr < b;
-  const float* ap = Y + (static_cast<int64_t>(j) * b + a0 + (aok ? lr : 0)) * ld + lk;
-  const float* bp = Y + (static_cast<int64_t>(t) * b + b0 + (bok ? lr : 0)) * ld + lk;
+  const float* ap = Y + row_of(j * b + a0 + (aok ? lr : 0)) * ld + lk;
+  const float* bp = Y + row_of(t * b + b0 + (bok ? lr : 0)) * ld + lk;
 
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   float acc[4][4] = {};
@@ -216,7 +233,7 @@ __device__ __forceinline__ void f32_tile(const float* __restrict__ Y, int64_t ld
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int col = b0 + tx * 4 + q;
-      if (col < b) Gj[row * ldg + static_cast<int64_t>(t) * b + col] = acc[u][q];
+      if (col < b) store_g<WT>(&Gj[row * ldg + static_cast<int64_t>(t) * b + col], acc[u][q]);
     }
   }
 }

@@ -45,13 +45,15 @@ hipError_t launch_gather(int storage, const void* Xs, const float* y, int64_t m,
 // Strictly-lower block triangle of Y Y^T in block-row layout, one 64 x 64
 // output tile per workgroup.
 // `order` (device, plan.slots ints) maps workgroups to tiles so that tiles
-// sharing rows of Y run on the same XCD; build it with gram_order.
+// sharing rows of Y run on the same XCD; build it with gram_order for the
+// number of XCDs the tiles are spread over (workgroup g of the Gram runs on
+// XCD g mod nx of those).
 constexpr int kXcds = 8;
 struct GramPlan {
   int tiles = 0;  // 64 x 64 output tiles
-  int slots = 0;  // workgroups launched: tiles rounded up to a multiple of kXcds
+  int slots = 0;  // workgroups launched: tiles rounded up to a multiple of nx
 };
-GramPlan gram_plan(int storage, int s, int b, int64_t ld);
+GramPlan gram_plan(int storage, int s, int b, int64_t ld, int nx = kXcds);
 // bf16 tile variant for rows of ld elements: 0 -> 32-wide K stages, one in
 // flight (ld <= 32); 1, 2, 3 -> 64-wide stages, 8, 4 or 2 in flight.
 inline int gram_variant(int64_t ld) {
@@ -59,7 +61,7 @@ inline int gram_variant(int64_t ld) {
   const int64_t nstage = (ld + 63) / 64;
   return nstage >= 8 ? 1 : nstage >= 4 ? 2 : 3;
 }
-std::vector<int> gram_order(int s, int b);
+std::vector<int> gram_order(int s, int b, int nx = kXcds);
 hipError_t launch_gram(int storage, const void* Y, int64_t ld, int s, int b, float* G,
                        const GramPlan& plan, const int* order, hipStream_t stream,
                        const LaunchTimer& tm = {});
@@ -86,26 +88,55 @@ struct ChainArgs {
   // Margins as tagged words (epoch, float) at vbox[row], written by other
   // workgroups of the same launch; nullptr: the chain computes them itself.
   const unsigned long long* vbox = nullptr;
+  // Chain workgroup q runs as workgroup q * stride of the launch.  With
+  // stride = the XCD count, dispatch places all of them on XCD 0, where the
+  // r values can travel through that XCD's L2 (see place).
+  int stride = 1;
+  // Q tagged words: the XCD of each chain workgroup, written at its start.
+  // When every chain workgroup finds all Q on its own XCD it publishes r with
+  // plain stores (they land in the shared L2, where the other workgroups'
+  // device-scope loads find them); otherwise, or with place == nullptr, with
+  // device-scope stores that write through to memory.
+  unsigned long long* place = nullptr;
+  // CUs of the device (host side only): a launch whose Q chain workgroups
+  // cannot all be resident at once fails with hipErrorLaunchOutOfResources
+  // instead of waiting on workgroups that never start.
+  int cus = 0;
 };
 // Whether chain workgroups of shape (s, b, Q, ld) run the fast recurrence
 // (the only one that can take its margins from vbox).
 bool chain_fast(int s, int b, int Q, int64_t ld);
 size_t chain_lds_bytes(int s, int b, int Q, int64_t ld);
-int chain_workgroups(int s, int b);
 constexpr int kChainMaxWorkgroups = 64;
+// How the recurrence's workgroups are laid out for a shape: Q workgroups at
+// launch indices q * stride.  one_xcd asks for all of them on one XCD (Q at
+// most cus_per_xcd); they must then all fit the fast recurrence path.
+struct ChainPlan {
+  int Q = 1;
+  int stride = 1;
+  bool lean = false;  // the shape runs the lean recurrence (launch_step)
+};
+ChainPlan chain_plan(int s, int b, int64_t ld, int xcds, int cus_per_xcd, int layout);
 hipError_t launch_chain(int storage, int loss, const ChainArgs& a, hipStream_t stream,
                         const LaunchTimer& tm = {});
 
-// One launch of the pipelined training loop: the chain of
-// outer step k on workgroups [0, a.Q), the margins of step k on
-// [mar0, mar0 + mar_wgs) (mar_wgs > 0; handed to the chain through a.vbox),
-// the Gram of step k+1 (gram_slots > 0)
-// on [gram0, gram0 + gram_slots) with gram0 a multiple of kXcds, and the
-// sample + gather of step k+2 (gath_wgs > 0) on [gath0, gath0 + gath_wgs).
-// The three roles use disjoint buffers; Y/G/yB of the chain, Y/G of the Gram
-// and idx/Y/yB of the gather belong to three different steps.
+// One launch of the pipelined training loop: the chain of outer step k on
+// the a.Q chain workgroups (see ChainArgs::stride), and on the other
+// workgroups the margins of step k (mar_wgs > 0; handed to the chain through
+// a.vbox), the Gram of step k+1 (gram_slots > 0; gram0 a multiple of the
+// number of XCDs the other roles run on, 8 or 7, so the tile order's XCD
+// grouping holds) and the sample + gather of step k+2 (gath_wgs > 0).  The
+// three roles use disjoint buffers; Y/G/yB of the chain, Y/G of the Gram and
+// idx/Y/yB of the gather belong to three different steps.
 struct PipeArgs {
   ChainArgs a;
+  // Non-chain roles are numbered o = 0, 1, ... over the workgroups that are
+  // not chain workgroups: with a.stride == 1 the chain is [0, Q) and o = w -
+  // ochain (ochain = Q rounded up to a multiple of 8); with a.stride == 8 the
+  // chain owns the multiples of 8 below 8Q, the other multiples of 8 exit at
+  // once, and o = 7 * (w / 8) + (w % 8) - 1 (XCDs 1..7).  The ranges below
+  // are in o.
+  int ochain = 0;
   int mar0 = 0, mar_wgs = 0, mar_rows = 0;  // margins: mar_rows rows per workgroup, into a.vbox
   unsigned long long* vbox_out = nullptr;   // = a.vbox, writable
   int gram0 = 0, gram_slots = 0, tps = 0;
@@ -124,6 +155,24 @@ struct PipeArgs {
 };
 hipError_t launch_pipe(int storage, int loss, const PipeArgs& p, hipStream_t stream,
                        const LaunchTimer& tm = {});
+
+// The same launch with the lean recurrence (casgd_step.h) for shapes where
+// step_fits holds (b a multiple of 4, at most 4 own rows per minibatch and 4
+// columns per lane, the workgroup's rows of G in LDS).  Needs the margins
+// role (mar_wgs > 0, a.vbox); a.preload is ignored.
+bool step_fits(int s, int b, int Q, int64_t ld);
+hipError_t launch_step(int storage, int loss, const PipeArgs& p, hipStream_t stream,
+                       const LaunchTimer& tm = {});
+
+// casgd_train's whole loop as one persistent launch of `grid` workgroups
+// (casgd_train.h); for shapes where step_fits holds.
+namespace persist {
+struct TrainArgs;
+}
+hipError_t launch_train(int storage, const persist::TrainArgs& A, int grid, hipStream_t stream,
+                        const LaunchTimer& tm = {});
+// Dynamic LDS bytes of that launch (0: it does not fit in one workgroup).
+size_t train_lds(int storage, int s, int b, int Q, int64_t ld, int mar_rows, bool dbl);
 
 // Lookahead form of the same kernel (one critical workgroup for the d latest
 // blocks of every step, M helpers for the rest, receivers for the update);

@@ -56,7 +56,8 @@ __host__ __device__ inline int fast_cols(int64_t nown_max, int64_t cpl) {
   return (nown_max == 1 && cpl == 1) ? 1 : (nown_max <= 2 && cpl <= 2) ? 2 : kMaxCpl;
 }
 
-constexpr int64_t kWlMax = 2048;  // w staged in LDS for ld up to this
+using chain::kWlMax;
+using chain::margins_wlds;
 
 struct ChainLayout {
   int64_t rs, vown, yown, acc, acc_len, region, region_len, wl, wl_len, total;
@@ -157,6 +158,7 @@ struct FastCtx {
   int64_t P;
   int *abort_flag, *r_ready, *acc_ready;
   const unsigned long long* mbox;
+  bool xl;  // every chain workgroup on this one's XCD: r goes out with plain stores
 };
 
 constexpr int kUpdRows = 4;  // rows per lane per block the update wave prefetches
@@ -279,7 +281,7 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
         const float zz = vj[t] - a.c * tot;
         const float rv = loss_deriv<LOSS>(zz, yj[t]);
         const uint64_t word = tagged(a.epoch, rv);
-        for (int dst = lane; dst < Q; dst += 64) chain::put(&a.xbuf[static_cast<int64_t>(dst) * sb + row], word);
+        for (int dst = lane; dst < Q; dst += 64) chain::put_x(&a.xbuf[static_cast<int64_t>(dst) * sb + row], word, x.xl);
         if (lane == 0) {
           a.z[row] = zz;
           a.r[row] = rv;
@@ -452,104 +454,6 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
   return upd;
 }
 
-// Margins x . w of the nrows own rows with w staged in LDS.  Every global
-// load of the first batch is issued before any is waited for: w (clamped
-// element loads, for the staging copy), the rows of Y, then whatever
-// `issued()` adds; w goes to LDS (zero past n) behind a workgroup barrier and
-// the dot products read it from there.  kRB rows per wave per batch; lane 0
-// calls out(p, row, value).  Called by the whole workgroup.
-template <typename T, typename RowOf, typename Out, typename Issued>
-__device__ __forceinline__ void margins_wlds(const T* Y, int64_t ld, int64_t n, const float* w, int nrows,
-                                             RowOf row_of, Out out, float* wl, Issued issued) {
-  constexpr int E = Elems<T>::E;
-  constexpr int kRB = 4;
-  constexpr int kWv = static_cast<int>(kWlMax / kThreads);  // w elements per thread
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int64_t cpr = ld / E;
-  float wtmp[kWv];
-#pragma unroll
-  for (int e = 0; e < kWv; ++e) {
-    const int64_t col = threadIdx.x + static_cast<int64_t>(kThreads) * e;
-    wtmp[e] = w[col < n ? col : n - 1];
-  }
-  // One batch: kRB rows of this wave, 4 chunks per lane from c0.  The first
-  // batch is separate code (FIRST), so no wait placed for the later batches
-  // can hold back the loads `issued()` adds to the first.
-  auto batch = [&](auto first_tag, int pass, int64_t c0, float (&acc)[kRB]) {
-    constexpr bool FIRST = decltype(first_tag)::value;
-    const int p0 = (pass * kWaves + wave) * kRB;
-    u32x4 qv[kRB][4];
-#pragma unroll
-    for (int r = 0; r < kRB; ++r) {
-      const int p = p0 + r;
-      const u32x4* yr = reinterpret_cast<const u32x4*>(Y + row_of(p < nrows ? p : 0) * ld);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t c = c0 + 64 * u;
-        qv[r][u] = yr[c < cpr ? c : 0];
-      }
-    }
-    if constexpr (FIRST) {
-      issued();
-      // the copies of w are touched only now, so no load above is waited
-      // for before every one of them is in flight
-#pragma unroll
-      for (int e = 0; e < kWv; ++e) asm volatile("" : "+v"(wtmp[e]) : : "memory");
-#pragma unroll
-      for (int e = 0; e < kWv; ++e) {
-        const int64_t col = threadIdx.x + static_cast<int64_t>(kThreads) * e;
-        if (col < ld) wl[col] = col < n ? wtmp[e] : 0.f;
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t c = c0 + 64 * u;
-      const f32x4* w4 = reinterpret_cast<const f32x4*>(wl + (c < cpr ? c : 0) * E);
-      float wv[E];
-#pragma unroll
-      for (int h = 0; h < E / 4; ++h) {
-        const f32x4 ww = w4[h];
-        wv[4 * h + 0] = ww.x;
-        wv[4 * h + 1] = ww.y;
-        wv[4 * h + 2] = ww.z;
-        wv[4 * h + 3] = ww.w;
-      }
-#pragma unroll
-      for (int r = 0; r < kRB; ++r) {
-        float f[E];
-        Elems<T>::widen(qv[r][u], f);
-        const bool on = p0 + r < nrows && c < cpr;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[r] = fmaf(f[e], on ? wv[e] : 0.f, acc[r]);
-      }
-    }
-  };
-  auto finish = [&](int pass, const float (&acc)[kRB]) {
-    const int p0 = (pass * kWaves + wave) * kRB;
-#pragma unroll
-    for (int r = 0; r < kRB; ++r) {
-      const float tot = group_sum<64>(acc[r]);
-      const int p = p0 + r;
-      if (lane == 0 && p < nrows) out(p, row_of(p), tot);
-    }
-  };
-  const int passes = (nrows + kWaves * kRB - 1) / (kWaves * kRB);
-  for (int pass = 0; pass < passes; ++pass) {
-    float acc[kRB];
-#pragma unroll
-    for (int r = 0; r < kRB; ++r) acc[r] = 0.f;
-    int64_t c0 = lane;
-    if (pass == 0) {
-      batch(std::integral_constant<bool, true>{}, 0, c0, acc);
-      c0 += 64 * 4;
-    }
-    for (; c0 < cpr; c0 += 64 * 4) batch(std::integral_constant<bool, false>{}, pass, c0, acc);
-    finish(pass, acc);
-  }
-}
-
 // The work of workgroup q (0 <= q < a.Q); called by all 256 lanes.
 template <typename T, int LOSS>
 __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
@@ -571,11 +475,19 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
   __shared__ int abort_flag;
   __shared__ int r_ready;                  // blocks whose r is in rs (wave 0)
   __shared__ int acc_ready[kWaves - 1];    // blocks folded into acc (waves 1..3)
+  __shared__ int xloc;                     // all chain workgroups on this XCD
   if (threadIdx.x == 0) {
     abort_flag = 0;
     r_ready = 0;
+    xloc = 0;
     for (int k = 0; k < kWaves - 1; ++k) acc_ready[k] = 0;
+    // where this workgroup runs, for the others' choice of store
+    if (a.place) chain::put(&a.place[q], tagged(a.epoch, __uint_as_float(chain::xcd_id())));
   }
+  // every chain workgroup's XCD, read early by wave 0 and checked below
+  uint64_t place_w = 0;
+  if (a.place && wave == 0)
+    place_w = __hip_atomic_load(&a.place[lane < Q ? lane : 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int64_t k = threadIdx.x; k < L.acc_len; k += kThreads) acc[k] = 0.f;
 
   const T* Y = static_cast<const T*>(a.Y);
@@ -637,13 +549,28 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
       gp.store<kGB>(tmp, g0, kThreads);
     }
   }
-  __syncthreads();  // vown, acc, flags and the G rows ready
+  if (a.place && wave == 0) {
+    // plain stores for r only if all Q chain workgroups share this XCD (a
+    // wait that expires counts as a mismatch and is reported)
+    const uint32_t mine = chain::xcd_id();
+    bool same = true;
+    if (lane < Q) {
+      uint32_t x = static_cast<uint32_t>(place_w);
+      if (static_cast<uint32_t>(place_w >> 32) != a.epoch)
+        x = __float_as_uint(chain::take(&a.place[lane], a.epoch, a.status, &abort_flag, 0, a.spin));
+      same = x == mine && !abort_flag;
+    }
+    const bool all = __all(same);
+    if (lane == 0) xloc = all ? 1 : 0;
+  }
+  __syncthreads();  // vown, acc, flags, the G rows and xloc ready
+  const bool xl = xloc != 0;
 
 
   const unsigned long long* mbox = a.xbuf + static_cast<int64_t>(q) * sb;
 
   if (fast) {
-    FastCtx x{&a, q, nown, nown_max, lane, wave, rs, vown, yown, acc, gl, P, &abort_flag, &r_ready, acc_ready, mbox};
+    FastCtx x{&a, q, nown, nown_max, lane, wave, rs, vown, yown, acc, gl, P, &abort_flag, &r_ready, acc_ready, mbox, xl};
     const int fc = fast_cols(nown_max, cpl);
     bool updated;
     if (fc == 1) updated = recurrence_fast<T, LOSS, 1, 1, 2>(x);
@@ -709,8 +636,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
           const uint64_t word = tagged(a.epoch, rv);
           // one copy per reader: each workgroup polls only its own mailbox
           for (int dst = lane; dst < Q; dst += 64)
-            __hip_atomic_store(&a.xbuf[static_cast<int64_t>(dst) * sb + row], word, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+            chain::put_x(&a.xbuf[static_cast<int64_t>(dst) * sb + row], word, xl);
           if (lane == 0) {
             a.z[row] = zz;
             a.r[row] = rv;
@@ -745,7 +671,9 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int q) {
 
 template <typename T, int LOSS>
 __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
-  chain_body<T, LOSS>(a, blockIdx.x);
+  const int w = blockIdx.x;
+  if (w % a.stride != 0) return;  // launch slots between chain workgroups
+  chain_body<T, LOSS>(a, w / a.stride);
 }
 
 // One launch of the pipelined training loop: the recurrence of outer step k
@@ -789,10 +717,22 @@ __device__ __forceinline__ void pipe_margins(const PipeArgs& p, int m, float* sm
 template <typename T, int LOSS, int BK, int D>
 __global__ __launch_bounds__(kThreads) void pipe_kernel(PipeArgs p) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
-  const int w = blockIdx.x;
-  if (w < p.a.Q) {
-    chain_body<T, LOSS>(p.a, w);
-    return;
+  const int wg = blockIdx.x;
+  int w;  // number among the non-chain workgroups
+  if (p.a.stride == 1) {
+    if (wg < p.a.Q) {
+      chain_body<T, LOSS>(p.a, wg);
+      return;
+    }
+    w = wg - p.ochain;
+    if (w < 0) return;
+  } else {
+    const int slot = wg / p.a.stride, x = wg % p.a.stride;
+    if (x == 0) {
+      if (slot < p.a.Q) chain_body<T, LOSS>(p.a, slot);
+      return;
+    }
+    w = slot * (p.a.stride - 1) + x - 1;
   }
   if (w >= p.mar0 && w < p.mar0 + p.mar_wgs) {
     pipe_margins<T>(p, w - p.mar0, sm);
@@ -821,6 +761,19 @@ __global__ __launch_bounds__(kThreads) void pipe_kernel(PipeArgs p) {
   }
 }
 
+// The chain workgroups wait for each other inside the launch, so all Q of
+// them must be resident at once: Q per XCD group of CUs (one XCD when they
+// are placed there, all CUs otherwise) times the kernel's occupancy.
+template <typename K>
+hipError_t check_resident(K kernel, size_t lds, const ChainArgs& a) {
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kernel),
+                                                              kThreads, lds);
+  if (e != hipSuccess) return e;
+  const int cus = a.stride > 1 ? a.cus / a.stride : a.cus;
+  return static_cast<int64_t>(occ) * cus >= a.Q ? hipSuccess : hipErrorLaunchOutOfResources;
+}
+
 template <typename T, int LOSS, int BK, int D>
 hipError_t pipe_t(const PipeArgs& p, int grid, size_t lds, hipStream_t st, const LaunchTimer& tm) {
   static size_t granted = 64 * 1024;
@@ -831,6 +784,8 @@ hipError_t pipe_t(const PipeArgs& p, int grid, size_t lds, hipStream_t st, const
     if (e != hipSuccess) return e;
     granted = lds;
   }
+  hipError_t e = check_resident(&pipe_kernel<T, LOSS, BK, D>, lds, p.a);
+  if (e != hipSuccess) return e;
   return launch_kernel(pipe_kernel<T, LOSS, BK, D>, dim3(grid), dim3(kThreads), lds, st, tm, p);
 }
 
@@ -856,7 +811,10 @@ hipError_t chain_t(const ChainArgs& a, size_t lds, hipStream_t st, const LaunchT
     if (e != hipSuccess) return e;
     granted = lds;
   }
-  return launch_kernel(chain_kernel<T, LOSS>, dim3(a.Q), dim3(kThreads), lds, st, tm, a);
+  hipError_t e = check_resident(&chain_kernel<T, LOSS>, lds, a);
+  if (e != hipSuccess) return e;
+  const int grid = a.stride * (a.Q - 1) + 1;
+  return launch_kernel(chain_kernel<T, LOSS>, dim3(grid), dim3(kThreads), lds, st, tm, a);
 }
 
 }  // namespace
@@ -875,16 +833,52 @@ size_t chain_lds_bytes(int s, int b, int Q, int64_t ld) {
   return need > kLdsReserve ? need : kLdsReserve;
 }
 
-int chain_workgroups(int s, int b) {
-  (void)s;
-  return b < kChainMaxWorkgroups ? b : kChainMaxWorkgroups;
+// Exact LDS of the chain workgroups, for launches whose other workgroups never
+// share an XCD with them.
+size_t chain_lds_need(int s, int b, int Q, int64_t ld) {
+  return static_cast<size_t>(chain_layout(s, b, Q, ld, chain_preload(s, b, Q, ld)).total) * sizeof(float);
+}
+
+// layout 0 picks the first that holds of: the lean recurrence on one XCD
+// (one workgroup per CU; an exchange round through one XCD's L2 costs a third
+// of one through memory, 0.4 against 1.2 us measured at 32 and 64
+// workgroups); the lean recurrence spread over the XCDs (one workgroup per
+// row up to 64); the general recurrence spread.  1 forces the spread form, 2
+// the one-XCD form with one workgroup per CU, 3 the one-XCD form with up to
+// two workgroups per CU.
+ChainPlan chain_plan(int s, int b, int64_t ld, int xcds, int cus_per_xcd, int layout) {
+  ChainPlan spread;
+  spread.Q = b < kChainMaxWorkgroups ? b : kChainMaxWorkgroups;
+  spread.stride = 1;
+  if (xcds <= 1) {
+    // one XCD in all: the same form, and the exchange is XCD-local anyway
+    spread.Q = b < cus_per_xcd ? b : cus_per_xcd;
+    spread.lean = step_fits(s, b, spread.Q, ld);
+    return spread;
+  }
+  spread.lean = step_fits(s, b, spread.Q, ld);
+  ChainPlan one;
+  one.Q = b < cus_per_xcd ? b : cus_per_xcd;
+  one.stride = xcds;
+  one.lean = step_fits(s, b, one.Q, ld);
+  ChainPlan two = one;
+  const int q2 = 2 * cus_per_xcd < kChainMaxWorkgroups ? 2 * cus_per_xcd : kChainMaxWorkgroups;
+  two.Q = b < q2 ? b : q2;
+  two.lean = step_fits(s, b, two.Q, ld);
+  if (layout == 1) return spread;
+  if (layout == 2) return one;
+  if (layout == 3) return two;
+  if (one.lean) return one;
+  return spread;
 }
 
 hipError_t launch_chain(int storage, int loss, const ChainArgs& a_in, hipStream_t st,
                         const LaunchTimer& tm) {
   ChainArgs a = a_in;
   a.preload = chain_preload(a.s, a.b, a.Q, a.ld) ? 1 : 0;
-  const size_t lds = chain_lds_bytes(a.s, a.b, a.Q, a.ld);
+  // spread over the XCDs: whole-CU LDS keeps other kernels off their CUs;
+  // packed on one XCD (possibly two per CU): their own LDS only
+  const size_t lds = a.stride == 1 ? chain_lds_bytes(a.s, a.b, a.Q, a.ld) : chain_lds_need(a.s, a.b, a.Q, a.ld);
   if (storage == kStoreBF16) {
     if (loss == kLogistic) return chain_t<uint16_t, kLogistic>(a, lds, st, tm);
     if (loss == kSquared) return chain_t<uint16_t, kSquared>(a, lds, st, tm);
@@ -898,14 +892,27 @@ hipError_t launch_chain(int storage, int loss, const ChainArgs& a_in, hipStream_
 hipError_t launch_pipe(int storage, int loss, const PipeArgs& p_in, hipStream_t st, const LaunchTimer& tm) {
   PipeArgs p = p_in;
   p.a.preload = chain_preload(p.a.s, p.a.b, p.a.Q, p.a.ld) ? 1 : 0;
-  size_t lds = chain_lds_bytes(p.a.s, p.a.b, p.a.Q, p.a.ld);
+  // Spread chain workgroups share XCDs with the other roles: whole-CU LDS
+  // keeps those off their CUs.  On their own XCD they need only their own.
+  size_t lds = p.a.stride == 1 ? chain_lds_bytes(p.a.s, p.a.b, p.a.Q, p.a.ld)
+                               : chain_lds_need(p.a.s, p.a.b, p.a.Q, p.a.ld);
   const size_t glds = storage != kStoreBF16 ? sizeof(float) * gram::kF32LdsElems
                       : sizeof(uint16_t) * (gram_variant(p.a.ld) == 0 ? gram::lds_elems<32>() : gram::lds_elems<64>());
   if (glds > lds) lds = glds;
-  int grid = p.a.Q;
-  if (p.mar_wgs > 0) grid = p.mar0 + p.mar_wgs;
-  if (p.gram_slots > 0) grid = p.gram0 + p.gram_slots;
-  if (p.gath_wgs > 0) grid = p.gath0 + p.gath_wgs;
+  // non-chain workgroups needed, in o numbering
+  int others = 0;
+  if (p.mar_wgs > 0) others = p.mar0 + p.mar_wgs;
+  if (p.gram_slots > 0) others = p.gram0 + p.gram_slots;
+  if (p.gath_wgs > 0) others = p.gath0 + p.gath_wgs;
+  int grid;
+  if (p.a.stride == 1) {
+    grid = others > 0 ? p.ochain + others : p.a.Q;
+  } else {
+    const int per = p.a.stride - 1;
+    const int slots_o = (others + per - 1) / per;
+    const int slots = slots_o > p.a.Q ? slots_o : p.a.Q;
+    grid = slots * p.a.stride;
+  }
   if (loss == kLogistic) return pipe_l<kLogistic>(storage, p, grid, lds, st, tm);
   if (loss == kSquared) return pipe_l<kSquared>(storage, p, grid, lds, st, tm);
   return pipe_l<kPoisson>(storage, p, grid, lds, st, tm);

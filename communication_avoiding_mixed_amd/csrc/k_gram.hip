@@ -40,25 +40,26 @@ __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-GramPlan gram_plan(int storage, int s, int b, int64_t ld) {
+GramPlan gram_plan(int storage, int s, int b, int64_t ld, int nx) {
   (void)storage;
   (void)ld;
   GramPlan p;
   const int tps = (b + kTile - 1) / kTile;
   p.tiles = s * (s - 1) / 2 * tps * tps;
-  p.slots = (p.tiles + kXcds - 1) / kXcds * kXcds;
+  p.slots = (p.tiles + nx - 1) / nx * nx;
   return p;
 }
 
 // Workgroups are dealt to the XCDs round-robin (workgroup w runs on XCD w mod
-// 8, each XCD with its own L2).  Tiles are listed in super-blocks of S x S
-// blocks (S chosen so a super-block holds about one XCD's share), the list is
-// cut into 8 consecutive runs, and run x is placed on the workgroups of XCD x:
-// the tiles that share rows of Y then share an L2.
-std::vector<int> gram_order(int s, int b) {
+// 8, each XCD with its own L2; in the pipelined step launch the Gram's
+// workgroups cycle over nx = 7 XCDs).  Tiles are listed in super-blocks of
+// S x S blocks (S chosen so a super-block holds about one XCD's share), the
+// list is cut into nx consecutive runs, and run x is placed on the workgroups
+// g with g mod nx = x: the tiles that share rows of Y then share an L2.
+std::vector<int> gram_order(int s, int b, int nx) {
   const int tps = (b + kTile - 1) / kTile;
   const int tiles = s * (s - 1) / 2 * tps * tps;
-  const int per = (tiles + kXcds - 1) / kXcds;
+  const int per = (tiles + nx - 1) / nx;
   int S = 1;
   while (S < s && (S + 1) * (S + 1) * tps * tps <= per) ++S;
   std::vector<int> list;
@@ -68,11 +69,11 @@ std::vector<int> gram_order(int s, int b) {
       for (int j = J * S; j < (J + 1) * S && j < s; ++j)
         for (int t = T * S; t < (T + 1) * S && t < j; ++t)
           for (int q = 0; q < tps * tps; ++q) list.push_back((j * (j - 1) / 2 + t) * tps * tps + q);
-  std::vector<int> order(static_cast<size_t>(per) * kXcds, -1);
-  for (int x = 0; x < kXcds; ++x)
+  std::vector<int> order(static_cast<size_t>(per) * nx, -1);
+  for (int x = 0; x < nx; ++x)
     for (int k = 0; k < per; ++k) {
       const int idx = x * per + k;
-      if (idx < tiles) order[static_cast<size_t>(k) * kXcds + x] = list[idx];
+      if (idx < tiles) order[static_cast<size_t>(k) * nx + x] = list[idx];
     }
   return order;
 }

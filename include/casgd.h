@@ -70,7 +70,8 @@ enum casgd_kernel_id {
   CASGD_K_CHAIN = 2,  /* margins + inner recurrence + weight update (one launch) */
   CASGD_K_PIPE = 3,   /* casgd_train's step launch: chain of step k, Gram of     */
                       /* step k+1 and gather of step k+2 together               */
-  CASGD_K_COUNT = 4
+  CASGD_K_TRAIN = 4,  /* casgd_train's single persistent launch of all steps    */
+  CASGD_K_COUNT = 5
 };
 
 /*
@@ -94,7 +95,11 @@ casgd_handle casgd_create(const float* X, const float* y, int64_t m, int64_t n,
 /* Free everything the handle owns.  NULL is allowed.  Synchronises its streams. */
 void casgd_destroy(casgd_handle h);
 
-/* Queue later work on hip_stream (a hipStream_t; NULL selects the null stream). */
+/* Queue later work on hip_stream (a hipStream_t; NULL selects the null
+ * stream).  When the stream changes, the new stream is first made to wait
+ * (an event, no host synchronisation) for everything already queued on the
+ * old one, since all work of a handle shares its buffers: switching streams
+ * never lets two of the handle's calls overlap. */
 int casgd_set_stream(casgd_handle h, void* hip_stream);
 
 /*
@@ -126,12 +131,20 @@ int casgd_outer_step_indices(casgd_handle h, int s, int b, float eta,
  * n_outer consecutive outer iterations; outer step k (k = first_step ...
  * first_step + n_outer - 1) samples with seed casgd_step_seed(base_seed, k).
  * Bit-identical to calling casgd_outer_step with those seeds.  Asynchronous.
- * With the default recurrence the loop is pipelined on the
- * handle's stream alone: after a prologue (gather and Gram of the first step,
- * gather of the second), each step is ONE launch that runs the margins,
- * recurrence and update of step k next to the Gram of step k+1 and the
- * gather of step k+2 (timer CASGD_K_PIPE).  Otherwise each step is queued as
- * by casgd_outer_step.
+ * With the default recurrence the loop runs on the handle's stream alone:
+ *   - for shapes the lean recurrence takes (see CASGD_OPT_TRAIN_FORM), ONE
+ *     persistent launch for all n_outer steps (timer CASGD_K_TRAIN): its
+ *     workgroups stay resident and hand results to each other, the Gram of
+ *     later steps running ahead of the recurrence; a small gather of the
+ *     last step follows so that casgd_debug_export sees that step's rows;
+ *   - otherwise, after a prologue (gather and Gram of the first step, gather
+ *     of the second), ONE launch per step that runs the margins, recurrence
+ *     and update of step k next to the Gram of step k+1 and the gather of
+ *     step k+2 (timer CASGD_K_PIPE).
+ * With the lookahead recurrence each step is queued as by casgd_outer_step.
+ * The persistent launch needs every one of its workgroups resident at once
+ * (one per CU); if the device cannot hold them the call fails with
+ * CASGD_EHIP before anything is queued.
  */
 int casgd_train(casgd_handle h, int s, int b, float eta, uint64_t base_seed,
                 uint64_t first_step, int n_outer, float* w);
@@ -198,7 +211,26 @@ enum casgd_option {
    *     (nearest, ties to even) when formed; the recurrence starts from the
    *     rounded value and CASGD_EXPORT_V returns it, widened to float.
    * Applies to every recurrence form and to casgd_train. */
-  CASGD_OPT_MARGIN_BF16 = 2
+  CASGD_OPT_MARGIN_BF16 = 2,
+  /* Placement of the all-to-all recurrence's workgroups (they exchange r
+   * at every inner step):
+   *   0 (default) on one XCD, whose shared L2 carries the exchange, whenever
+   *     the shape allows it (at most 4 rows per minibatch per workgroup with
+   *     one workgroup per CU of that XCD), else spread over all XCDs;
+   *   1 spread over all XCDs, one workgroup per row up to 64;
+   *   2 on one XCD whatever the shape.
+   * A launch whose recurrence workgroups cannot all be resident at once
+   * fails with CASGD_EHIP.  Results depend on the layout only through the
+   * float32 summation order of the weight update. */
+  CASGD_OPT_CHAIN_LAYOUT = 3,
+  /* How casgd_train runs its steps:
+   *   0 (default) one persistent launch for all steps whenever the shape
+   *     runs the lean recurrence (b a multiple of 4, at most 4 rows per
+   *     minibatch per recurrence workgroup and 4 columns per lane, the
+   *     workgroup's rows of G in LDS), else one launch per step;
+   *   1 one launch per step.
+   * Both give bit-identical results. */
+  CASGD_OPT_TRAIN_FORM = 4
 };
 
 /* Set an option of the handle; later outer steps use it.  EINVAL for an

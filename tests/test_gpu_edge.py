@@ -201,12 +201,14 @@ def test_lookahead_repeatable_and_resumable():
     assert torch.equal(w1, w2)
 
 
-def test_side_stream_and_timing():
+@pytest.mark.parametrize("form", [B.TRAIN_PERSISTENT, B.TRAIN_PER_STEP])
+def test_side_stream_and_timing(form):
     import torch
     name = "logistic-4096x64"
     wl = synth.WORKLOADS[name]
     X, y = synth.make_data(name)
     h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss)
+    h.set_option(B.OPT_TRAIN_FORM, form)
     w_ref = torch.zeros(wl.n, device="cuda")
     h.train(wl.s, wl.b, wl.eta, 0, 0, 5, w_ref)
     side = torch.cuda.Stream()
@@ -216,12 +218,47 @@ def test_side_stream_and_timing():
         h.train(wl.s, wl.b, wl.eta, 0, 0, 5, w)
         ms, cnt = h.timing(B.K_PIPE)
         g_ms, g_cnt = h.timing(B.K_GRAM)
+        t_ms, t_cnt = h.timing(B.K_TRAIN)
         h.set_timing(False)
     side.synchronize()
     assert torch.equal(w, w_ref)
-    # pipelined: one stand-alone Gram (the first step's), then one launch per step
-    assert cnt == 5 and ms > 0
-    assert g_cnt == 1 and g_ms > 0
+    if form == B.TRAIN_PERSISTENT:
+        # one launch for all five steps
+        assert t_cnt == 1 and t_ms > 0 and cnt == 0 and g_cnt == 0
+    else:
+        # one stand-alone Gram (the first step's), then one launch per step
+        assert cnt == 5 and ms > 0
+        assert g_cnt == 1 and g_ms > 0 and t_cnt == 0
+
+
+def test_train_forms_bit_identical():
+    """The persistent launch and one launch per step give the same bits, and
+    both equal outer steps queued one by one, for every lean variant."""
+    import torch
+    for s, b, Q_note in ((4, 16, "1 row"), (6, 64, "2 rows"), (5, 128, "2 rows, 2 columns"),
+                         (3, 256, "4 rows, 4 columns")):
+        n = 300
+        X = synth.make_uniform((5000, n), seed=s * 100 + b, lo=-0.1, hi=0.1)
+        y = np.sign(synth.make_uniform(5000, seed=b)).astype(np.float32)
+        y[y == 0] = 1.0
+        h = B.CASGD(torch_dev(X), torch_dev(y), "logistic")
+        outs = []
+        for form in (B.TRAIN_PERSISTENT, B.TRAIN_PER_STEP):
+            h.set_option(B.OPT_TRAIN_FORM, form)
+            w = torch_dev(synth.make_w0("epsilon", 3, n=n) * 0.05)
+            h.train(s, b, 0.5, 11, 2, 7, w)
+            outs.append((w.clone(), h.export(B.EXPORT_R), h.export(B.EXPORT_V), h.export(B.EXPORT_G),
+                         h.export(B.EXPORT_IDX)))
+        w = torch_dev(synth.make_w0("epsilon", 3, n=n) * 0.05)
+        for k in range(2, 9):
+            h.outer_step(s, b, 0.5, B.step_seed(11, k), w)
+        outs.append((w.clone(), h.export(B.EXPORT_R), h.export(B.EXPORT_V), h.export(B.EXPORT_G),
+                     h.export(B.EXPORT_IDX)))
+        for o in outs[1:]:
+            assert torch.equal(outs[0][0], o[0]), (s, b, Q_note)
+            for a, c in zip(outs[0][1:], o[1:]):
+                assert np.array_equal(a, c), (s, b, Q_note)
+        h.close()
 
 
 @pytest.mark.parametrize("rec", [B.RECURRENCE_ALL_TO_ALL, B.RECURRENCE_LOOKAHEAD])

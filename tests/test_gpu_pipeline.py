@@ -1,7 +1,8 @@
-"""casgd_train's pipelined loop (one launch per outer step: recurrence of step
-k, Gram of step k+1, gather of step k+2) against the same steps queued one by
-one with casgd_outer_step: weights and every exported intermediate must be
-bit-identical, since both run the same device code on the same inputs."""
+"""casgd_train in both of its forms (one persistent launch for all steps, and
+one launch per outer step: recurrence of step k, Gram of step k+1, gather of
+step k+2) against the same steps queued one by one with casgd_outer_step:
+weights and every exported intermediate must be bit-identical, since all run
+the same device code on the same inputs."""
 
 import numpy as np
 import pytest
@@ -15,6 +16,7 @@ from gpu_common import REL_TOL, rel_l2, torch_dev
 pytestmark = pytest.mark.gpu
 
 EXPORTS = (B.EXPORT_IDX, B.EXPORT_Y, B.EXPORT_YB, B.EXPORT_G, B.EXPORT_V, B.EXPORT_Z, B.EXPORT_R)
+FORMS = [B.TRAIN_PERSISTENT, B.TRAIN_PER_STEP]
 
 
 def _data(loss, m, n, seed):
@@ -29,6 +31,7 @@ def _data(loss, m, n, seed):
     return X, y
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("loss", ["logistic", "squared", "poisson"])
 @pytest.mark.parametrize("m,n,s,b,n_outer", [
     (3000, 300, 4, 64, 5),    # several tiles, whole pipeline
@@ -44,12 +47,13 @@ def _data(loss, m, n, seed):
     (4000, 512, 8, 256, 2),   # synth-like: 4 rows per workgroup, 4 columns per lane
     (2000, 64, 40, 64, 2),    # one row per workgroup with G too large for LDS
 ])
-def test_train_equals_outer_steps(loss, m, n, s, b, n_outer):
+def test_train_equals_outer_steps(form, loss, m, n, s, b, n_outer):
     import torch
     X, y = _data(loss, m, n, seed=m + s)
     eta = 0.3 if loss != "poisson" else 0.05
     base, first = 11, 5
     h = B.CASGD(torch_dev(X), torch_dev(y), loss)
+    h.set_option(B.OPT_TRAIN_FORM, form)
     w_pipe = torch_dev(synth.make_uniform((n,), seed=2, lo=-0.2, hi=0.2))
     w_step = w_pipe.clone()
     h.train(s, b, eta, base, first, n_outer, w_pipe)
@@ -62,11 +66,13 @@ def test_train_equals_outer_steps(loss, m, n, s, b, n_outer):
         assert np.array_equal(got[k], h.export(k)), k
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("m,n,s,b,n_outer", [(1500, 45, 5, 24, 4), (1000, 300, 3, 64, 3), (600, 20, 1, 32, 5)])
-def test_train_equals_outer_steps_fp32(m, n, s, b, n_outer):
+def test_train_equals_outer_steps_fp32(form, m, n, s, b, n_outer):
     import torch
     X, y = _data("logistic", m, n, seed=m)
     h = B.CASGD(torch_dev(X), torch_dev(y), "logistic", "fp32")
+    h.set_option(B.OPT_TRAIN_FORM, form)
     w_pipe = torch_dev(synth.make_uniform((n,), seed=4, lo=-0.2, hi=0.2))
     w_step = w_pipe.clone()
     h.train(s, b, 0.4, 3, 0, n_outer, w_pipe)
@@ -79,12 +85,14 @@ def test_train_equals_outer_steps_fp32(m, n, s, b, n_outer):
         assert np.array_equal(got[k], h.export(k)), k
 
 
-def test_train_then_steps_interleave():
+@pytest.mark.parametrize("form", FORMS)
+def test_train_then_steps_interleave(form):
     import torch
     name = "logistic-4096x64"
     wl = synth.WORKLOADS[name]
     X, y = synth.make_data(name)
     h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss)
+    h.set_option(B.OPT_TRAIN_FORM, form)
     w1 = torch.zeros(wl.n, device="cuda")
     h.outer_step(wl.s, wl.b, wl.eta, O.step_seed(0, 0), w1)
     h.train(wl.s, wl.b, wl.eta, 0, 1, 6, w1)
@@ -97,13 +105,15 @@ def test_train_then_steps_interleave():
     assert torch.equal(w1, w2)
 
 
-def test_pipelined_step_against_oracle():
-    """The last step of a pipelined run, from the GPU's own w0, to the bar."""
+@pytest.mark.parametrize("form", FORMS)
+def test_pipelined_step_against_oracle(form):
+    """The last step of a training run, from the GPU's own w0, to the bar."""
     import torch
     name = "epsilon"
     wl = synth.WORKLOADS[name]
     X, y = synth.make_data(name, m=20_000)
     h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss)
+    h.set_option(B.OPT_TRAIN_FORM, form)
     w = torch.zeros(wl.n, device="cuda")
     h.train(wl.s, wl.b, wl.eta, 0, 0, 3, w)
     w0 = w.clone()
@@ -122,6 +132,7 @@ def test_pipe_timer_counts_launches():
     wl = synth.WORKLOADS[name]
     X, y = synth.make_data(name)
     h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss)
+    h.set_option(B.OPT_TRAIN_FORM, B.TRAIN_PER_STEP)
     w = torch.zeros(wl.n, device="cuda")
     h.set_timing(True)
     h.train(wl.s, wl.b, wl.eta, 0, 0, 7, w)
@@ -132,12 +143,28 @@ def test_pipe_timer_counts_launches():
     assert g_cnt == 2  # prologue: steps 0 and 1
 
 
+def test_train_timer_counts_one_launch():
+    import torch
+    name = "logistic-4096x64"
+    wl = synth.WORKLOADS[name]
+    X, y = synth.make_data(name)
+    h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss)
+    w = torch.zeros(wl.n, device="cuda")
+    h.set_timing(True)
+    h.train(wl.s, wl.b, wl.eta, 0, 0, 7, w)
+    ms, cnt = h.timing(B.K_TRAIN)
+    p_ms, p_cnt = h.timing(B.K_PIPE)
+    h.set_timing(False)
+    assert cnt == 1 and ms > 0 and p_cnt == 0
+
+
 def test_sampled_timing_stamps_every_kth_launch():
     import torch
     name = "logistic-4096x64"
     wl = synth.WORKLOADS[name]
     X, y = synth.make_data(name)
     h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss)
+    h.set_option(B.OPT_TRAIN_FORM, B.TRAIN_PER_STEP)
     w = torch.zeros(wl.n, device="cuda")
     h.set_timing(True, every=3)
     h.train(wl.s, wl.b, wl.eta, 0, 0, 10, w)
