@@ -50,6 +50,8 @@ SIGNATURES = {
                               ctypes.POINTER(ctypes.c_int64), _I]),
     "casgd_last_error": (ctypes.c_char_p, []),
     "casgd_set_option": (_I, [_VP, _I, _I]),
+    "casgd_peak_copy": (_I, [_VP, _VP, _I64, _VP]),
+    "casgd_peak_mfma": (_I, [_VP, _I, _I, _VP]),
 }
 
 _lib = None
@@ -103,6 +105,30 @@ def _dev_f32(t, shape, name):
     if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def peak_copy(src, dst):
+    """Copy src into dst (same byte size) with the calibration copy kernel, on
+    torch's current stream; returns the bytes read (= bytes written)."""
+    import torch
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same byte size")
+    _check(load().casgd_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                  nbytes, _stream_ptr()), "casgd_peak_copy")
+    return nbytes
+
+
+def peak_mfma(out, workgroups: int, iters: int):
+    """Run the MFMA calibration loop on torch's current stream; out is a
+    float32 GPU tensor of workgroups * 256 elements.  Returns its flops."""
+    _dev_f32(out, (workgroups * 256,), "out")
+    _check(load().casgd_peak_mfma(ctypes.c_void_p(out.data_ptr()), workgroups, iters, _stream_ptr()),
+           "casgd_peak_mfma")
+    return workgroups * 4 * 4 * iters * 2 * 32 * 32 * 16
 
 
 class CASGD:

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libcasgd.so")
 
 SOURCES = ["casgd_api.hip", "k_gather.hip", "k_gram.hip", "k_chain.hip", "k_chain_la.hip", "k_loss.hip",
            "k_step.hip", "k_step_1x1.hip", "k_step_2x1.hip", "k_step_2x2.hip", "k_step_4x2.hip",
-           "k_step_4x4.hip"]
+           "k_step_4x4.hip", "k_peak.hip"]
 HEADERS = ["casgd_device.h", "casgd_internal.h", "casgd_chain.h"]
 
 ARCH = "gfx950"

@@ -612,6 +612,30 @@ extern "C" {
 
 const char* casgd_last_error(void) { return g_last_error.c_str(); }
 
+int casgd_peak_copy(const void* src, void* dst, int64_t bytes, void* hip_stream) {
+  if (!src || !dst) return fail(CASGD_EINVAL, "NULL pointer");
+  if (bytes < 0 || bytes % 16 != 0) return fail(CASGD_EINVAL, "bytes must be a non-negative multiple of 16");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+    return fail(CASGD_EINVAL, "src and dst must be 16-byte aligned");
+  const char* a = static_cast<const char*>(src);
+  const char* d = static_cast<const char*>(dst);
+  if (a < d + bytes && d < a + bytes) return fail(CASGD_EINVAL, "src and dst overlap");
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "querying the compute unit count");
+  e = casgd::launch_peak_copy(src, dst, bytes, cus, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? CASGD_OK : hip_fail(e, "copy calibration launch");
+}
+
+int casgd_peak_mfma(float* out, int workgroups, int iters, void* hip_stream) {
+  if (!out) return fail(CASGD_EINVAL, "NULL pointer");
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1)
+    return fail(CASGD_EINVAL, "workgroups must be in [1, 2^20] and iters >= 1");
+  hipError_t e = casgd::launch_peak_mfma(out, workgroups, iters, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? CASGD_OK : hip_fail(e, "MFMA calibration launch");
+}
+
 uint64_t casgd_step_seed(uint64_t base_seed, uint64_t k) { return casgd::splitmix64(base_seed, k); }
 
 int64_t casgd_gram_bytes(int s, int b, int packed) {

@@ -194,4 +194,10 @@ hipError_t launch_loss(int storage, int loss, const void* Xs, const float* y, in
                        int64_t n, int64_t ld, const float* w, double* partial, double* out_dev,
                        hipStream_t stream);
 
+// Calibration kernels (k_peak.hip): a copy of bytes (a multiple of 16) from
+// src to dst, and workgroups x 256 lanes of iters x 4 dependent bf16 MFMAs
+// (32x32x16) per wave, each lane's accumulator sum written to out.
+hipError_t launch_peak_copy(const void* src, void* dst, int64_t bytes, int cus, hipStream_t stream);
+hipError_t launch_peak_mfma(float* out, int workgroups, int iters, hipStream_t stream);
+
 }  // namespace casgd

@@ -249,6 +249,23 @@ int casgd_set_timing(casgd_handle h, int on);
 int casgd_get_timing(casgd_handle h, int kernel, double* total_ms, int64_t* launches,
                      int reset);
 
+/* Calibration kernels for roofline reporting (not part of the method).
+ *
+ * casgd_peak_copy: copy `bytes` (a multiple of 16) from device src to device
+ * dst, both 16-byte aligned and not overlapping, with a plain grid-stride
+ * kernel on hip_stream (NULL: the null stream).  It reads and writes `bytes`
+ * each: the achievable HBM rate, and a kernel of known traffic that scales
+ * the HBM byte counters.  EINVAL for bad sizes, alignment or overlap.
+ *
+ * casgd_peak_mfma: launch `workgroups` workgroups of 256 lanes; each wave
+ * runs iters x 4 bf16 MFMAs (32x32x16, float32 accumulators) on four
+ * independent accumulator chains and each lane stores its accumulator sum to
+ * device out[workgroups * 256].  It does workgroups * 4 waves * 4 chains *
+ * iters * 32768 flops: the achievable dense bf16 matrix-core rate under
+ * sustained load.  EINVAL for workgroups outside [1, 2^20] or iters < 1. */
+int casgd_peak_copy(const void* src, void* dst, int64_t bytes, void* hip_stream);
+int casgd_peak_mfma(float* out, int workgroups, int iters, void* hip_stream);
+
 /* Text of the last error on the calling thread ("" if none). */
 const char* casgd_last_error(void);
 
