@@ -50,6 +50,7 @@ SIGNATURES = {
                               ctypes.POINTER(ctypes.c_int64), _I]),
     "casgd_last_error": (ctypes.c_char_p, []),
     "casgd_set_option": (_I, [_VP, _I, _I]),
+    "casgd_loss_noalloc": (_I, [_VP, _VP, _VP]),
     "casgd_peak_copy": (_I, [_VP, _VP, _I64, _VP]),
     "casgd_peak_mfma": (_I, [_VP, _I, _I, _VP]),
 }

@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -24,9 +25,35 @@
 #include "casgd_internal.h"
 #include "casgd_train.h"
 
+// Static scratch of casgd_loss_noalloc: the loss reduction's per-workgroup
+// partial sums.  Each GPU the library runs on holds its own copy until the
+// process ends; every call on that GPU shares it.  Host code never uses this
+// name as an address: the device address comes from hipGetSymbolAddress.
+constexpr int kNoAllocPartials = casgd::kLossBlocks;
+static __device__ __align__(256) double scratch[kNoAllocPartials];
+
 namespace {
 
 thread_local std::string g_last_error;
+
+// device address of `scratch` per device id, resolved once per device
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_addr;
+
+// With dev current: the address of its copy of `scratch`.
+hipError_t scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (dev < 0) return hipErrorInvalidDevice;
+  if (static_cast<int>(g_scratch_addr.size()) <= dev) g_scratch_addr.resize(dev + 1, nullptr);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
 
 int fail(int code, const std::string& msg) {
   g_last_error = msg;
@@ -89,6 +116,7 @@ struct casgd_ctx {
   int* status = nullptr;
   double* loss_partial = nullptr;
   double* loss_out = nullptr;
+  double* scratch = nullptr;  // this device's copy of the static scratch (casgd_loss_noalloc)
   uint32_t epoch = 0;
   int recurrence = 0;  // CASGD_OPT_RECURRENCE
   long spin = 0;       // CASGD_OPT_SPIN_LIMIT (0: the default bound)
@@ -685,6 +713,9 @@ casgd_handle casgd_create(const float* X, const float* y, int64_t m, int64_t n, 
   }
   h->xcds = xcds >= 1 && cus % xcds == 0 ? xcds : 1;
   h->cus = cus >= 1 ? cus : 1;
+  void* scratch_ptr = nullptr;
+  ok = ok && scratch_address(dev, &scratch_ptr) == hipSuccess;
+  h->scratch = static_cast<double*>(scratch_ptr);
   if (!ok) {
     (void)hipGetLastError();
     fail(CASGD_EHIP, "creating the handle's stream and events failed");
@@ -843,6 +874,20 @@ int casgd_loss(casgd_handle h, const float* w, double* out) {
   if (e == hipSuccess) e = sync_all(h);
   if (e != hipSuccess) return hip_fail(e, "loss");
   return check_status(h);
+}
+
+int casgd_loss_noalloc(casgd_handle h, const float* w, double* out_dev) {
+  if (!h) return fail(CASGD_EINVAL, "NULL handle");
+  if (!w || !out_dev) return fail(CASGD_EINVAL, "NULL pointer");
+  if (!h->scratch) return fail(CASGD_EHIP, "the static scratch has no device address");
+  const int np = casgd::loss_partials(h->storage, h->m, h->ld);
+  if (np > kNoAllocPartials)
+    return fail(CASGD_EINVAL, "the loss needs " + std::to_string(np) + " partial sums; the static scratch holds " +
+                                  std::to_string(kNoAllocPartials));
+  const hipError_t e = casgd::launch_loss(h->storage, h->loss, h->Xs, h->y, h->m, h->n, h->ld, w, h->scratch,
+                                          out_dev, h->stream);
+  if (e != hipSuccess) return hip_fail(e, "loss launch");
+  return CASGD_OK;
 }
 
 int casgd_debug_export(casgd_handle h, int what, void* dst, size_t bytes) {

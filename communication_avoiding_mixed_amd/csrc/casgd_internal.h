@@ -193,6 +193,8 @@ constexpr int kLossBlocks = 2048;
 hipError_t launch_loss(int storage, int loss, const void* Xs, const float* y, int64_t m,
                        int64_t n, int64_t ld, const float* w, double* partial, double* out_dev,
                        hipStream_t stream);
+// The partial sums launch_loss writes for this shape (at most kLossBlocks).
+int loss_partials(int storage, int64_t m, int64_t ld);
 
 // Calibration kernels (k_peak.hip): a copy of bytes (a multiple of 16) from
 // src to dst, and workgroups x 256 lanes of iters x 4 dependent bf16 MFMAs

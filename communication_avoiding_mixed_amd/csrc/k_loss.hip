@@ -202,6 +202,9 @@ inline int narrow_blocks(int64_t m) {
   return static_cast<int>(need < kLossBlocks ? need : kLossBlocks);
 }
 
+// Partial sums of the loss kernel for rows of cpr 16-byte chunks.
+inline int partials_for(int64_t cpr, int64_t m) { return cpr > 8 ? kLossBlocks : narrow_blocks(m); }
+
 // Launches the loss kernel for this row width; returns the partial sums it writes.
 template <typename T, int LOSS>
 int loss_gs(const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld, const float* w,
@@ -220,7 +223,7 @@ int loss_gs(const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld, co
     loss_narrow_kernel<T, LOSS, 8><<<narrow_blocks(m), 256, 0, st>>>(X, y, m, n, ld, w, partial);
   else
     loss_narrow_kernel<T, LOSS, 4><<<narrow_blocks(m), 256, 0, st>>>(X, y, m, n, ld, w, partial);
-  return cpr > 8 ? kLossBlocks : narrow_blocks(m);
+  return partials_for(cpr, m);
 }
 
 template <typename T>
@@ -232,6 +235,11 @@ int loss_t(int loss, const void* Xs, const float* y, int64_t m, int64_t n, int64
 }
 
 }  // namespace
+
+int loss_partials(int storage, int64_t m, int64_t ld) {
+  const int64_t cpr = storage == kStoreBF16 ? ld / Widen<uint16_t>::kElems : ld / Widen<float>::kElems;
+  return partials_for(cpr, m);
+}
 
 hipError_t launch_loss(int storage, int loss, const void* Xs, const float* y, int64_t m, int64_t n,
                        int64_t ld, const float* w, double* partial, double* out_dev,

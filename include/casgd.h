@@ -161,6 +161,22 @@ uint64_t casgd_step_seed(uint64_t base_seed, uint64_t k);
  */
 int casgd_loss(casgd_handle h, const float* w, double* out);
 
+/* casgd_loss for callers that cannot allocate or wait: code under HIP graph
+ * capture, allocation-free serving and training loops, harnesses that forbid
+ * hipMalloc.  The same mean loss f(w) as casgd_loss (the same kernels and
+ * summation order, so the same bits), written to *out_dev (one device double)
+ * on the handle's stream; returns without waiting.  Allocates nothing: the
+ * per-workgroup partial sums go to a static device array of the library
+ * holding 2048 doubles (16 KiB) per GPU, kept by each GPU the library runs on
+ * until the process ends.  A shape whose reduction would need more partial
+ * sums than that is refused with EINVAL (the loss uses at most 2048, so no
+ * handle's shape is refused today).  Every call on one GPU shares that array:
+ * calls that overlap on one GPU (other streams, other handles, other threads)
+ * race and may return wrong values.  Every partial sum a call reads is written
+ * by that call first, so nothing is cleared.  EINVAL for a NULL handle or
+ * pointer. */
+int casgd_loss_noalloc(casgd_handle h, const float* w, double* out_dev);
+
 /*
  * Copy part of the most recent outer step's state to host memory (tests and
  * benchmarks).  what: enum casgd_export_what; bytes must equal the exact size
