@@ -4,11 +4,14 @@ This module only draws data: it holds none of the method's arithmetic (no
 rounding to low precision, no sampling of minibatches, no losses).  Both the
 HIP path and the CPU oracle take its float32 arrays as their common input.
 
-The five workloads follow the shapes of the data sets named in the Abstract of
+The workloads follow the shapes of the data sets named in the Abstract of
 "Mixed-Precision Communication-Avoiding SGD for Generalized Linear Models on
-GPUs" (epsilon, HIGGS, synth, Poisson-synth) plus one small logistic case.  The
-real data sets are not available here; these stand in for them with the same
-row and column counts and a comparable value structure.
+GPUs" (epsilon, SUSY, HIGGS, synth, Poisson-synth) plus one small logistic
+case.  The real data sets are not available here; these stand in for them with
+the same row and column counts and a comparable value structure.  The page
+gives no shape for SUSY: it is taken as the public data set's 5,000,000 rows of
+18 features, run with the HIGGS-shaped case's s, b and eta (both are tall,
+narrow logistic problems).
 
 Recipe (all draws from numpy's PCG64 generator seeded with `seed`, in this
 order: X as float32, then w* as float64, then noise / label flips / counts):
@@ -19,6 +22,9 @@ order: X as float32, then w* as float64, then noise / label flips / counts):
   higgs             even columns N(0, 1), odd columns lognormal(0, 0.5), each
                     column standardised (float64 mean, population std);
                     y = sign(X w*) with 25% flipped
+  susy              columns 0-7 N(0, 1), columns 8-17 lognormal(0, 0.5), each
+                    column standardised as for higgs; y = sign(X w*) with 20%
+                    flipped
   synth-lsq         X ~ N(0, 1/512); y = X w* + N(0, 0.01^2)
   poisson-synth     X ~ 0.5 * N(0, 1/256); y ~ Poisson(exp(X w*))
 
@@ -54,6 +60,8 @@ WORKLOADS = {
     "epsilon": Workload("epsilon", 400_000, 2000, 16, 64, 1.0, "logistic", 200),
     "higgs": Workload("higgs", 11_000_000, 28, 32, 128, 0.1, "logistic", 200,
                       w0_scale=float(1.0 / np.sqrt(28.0))),
+    "susy": Workload("susy", 5_000_000, 18, 32, 128, 0.1, "logistic", 200,
+                     w0_scale=float(1.0 / np.sqrt(18.0))),
     "synth-lsq": Workload("synth-lsq", 1_000_000, 512, 8, 256, 0.05, "squared", 200),
     "poisson-synth": Workload("poisson-synth", 2_000_000, 256, 16, 128, 0.01, "poisson", 200),
 }
@@ -93,12 +101,14 @@ def make_data(name: str, seed: int = 0, m: int | None = None):
             Xc = X[a:a + _CHUNK].astype(np.float64)
             Xc /= np.sqrt(np.sum(Xc * Xc, axis=1))[:, None]
             X[a:a + _CHUNK] = Xc.astype(np.float32)
-    elif name == "higgs":
+    elif name in ("higgs", "susy"):
         X = np.empty((m, n), dtype=np.float32)
-        even = np.arange(0, n, 2)
-        odd = np.arange(1, n, 2)
-        X[:, even] = rng.standard_normal((m, even.size), dtype=np.float32)
-        X[:, odd] = rng.lognormal(0.0, 0.5, (m, odd.size)).astype(np.float32)
+        if name == "higgs":
+            normal, skewed = np.arange(0, n, 2), np.arange(1, n, 2)
+        else:
+            normal, skewed = np.arange(0, 8), np.arange(8, n)
+        X[:, normal] = rng.standard_normal((m, normal.size), dtype=np.float32)
+        X[:, skewed] = rng.lognormal(0.0, 0.5, (m, skewed.size)).astype(np.float32)
         for c in range(n):
             col = X[:, c].astype(np.float64)
             mu = col.mean()
@@ -120,6 +130,8 @@ def make_data(name: str, seed: int = 0, m: int | None = None):
         y = _signs_with_flips(rng, margins, 0.10)
     elif name == "higgs":
         y = _signs_with_flips(rng, margins, 0.25)
+    elif name == "susy":
+        y = _signs_with_flips(rng, margins, 0.20)
     elif name == "synth-lsq":
         y = (margins + 0.01 * rng.standard_normal(m)).astype(np.float32)
     else:

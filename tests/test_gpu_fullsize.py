@@ -102,3 +102,44 @@ def test_full_size_workload(name):
           f"({flips} rows off the nearest rounding), final loss {f_mix:.6f} gap {gap_mix:.2e}", flush=True)
     assert gap_mix <= LOSS_GAP
     h.close()
+
+
+def test_fp32_sgd_baseline_at_epsilon_shape():
+    """The plain SGD the benchmark's speedup divides by: casgd_train with
+    s = 1 on float32-stored data, epsilon shape (400000 x 2000, b = 64,
+    eta = 1), base seed 7, in the launch configuration the benchmark times.
+    Each of the first steps, from the GPU's own weights, against the
+    oracle's step on the float32 values (v, r and w within relative L2
+    1e-4); then the benchmark's whole run (5 x 16 warm-up steps, then
+    200 x 16 steps) ending within 0.5% of the loss of the oracle's float64
+    SGD over the same minibatches."""
+    import torch
+    name = "epsilon"
+    wl = synth.WORKLOADS[name]
+    X, y = synth.make_data(name)
+    h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss, "fp32")
+    w = torch.zeros(wl.n, device="cuda")
+    for k in range(12):
+        w0 = w.cpu().numpy().astype(np.float64)
+        h.train(1, wl.b, wl.eta, 7, k, 1, w)
+        ref = O.outer_step(X, y, w0, 1, wl.b, wl.eta, O.step_seed(7, k), wl.loss, storage="fp32")
+        assert np.array_equal(h.export(B.EXPORT_IDX).astype(np.int64), ref["idx"]), k
+        errs = {"v": rel_l2(h.export(B.EXPORT_V), ref["v"]), "r": rel_l2(h.export(B.EXPORT_R), ref["r"]),
+                "w": rel_l2(w.cpu().numpy(), ref["w"])}
+        for key, e in errs.items():
+            assert e <= REL_TOL, (k, key, e)
+
+    warm, timed = 5 * wl.s, 200 * wl.s
+    wt = torch.zeros(wl.n, device="cuda")
+    h.train(1, wl.b, wl.eta, 7, 0, warm, wt)
+    h.train(1, wl.b, wl.eta, 7, warm, timed, wt)
+    f_gpu = h.loss_value(wt)
+    w_sgd = O.train(X, y, np.zeros(wl.n), 1, wl.b, wl.eta, wl.loss, base_seed=7, n_outer=warm + timed,
+                    storage="fp32", method="sgd")
+    f_ref = O.full_loss(X, y, w_sgd, wl.loss, storage="fp32")
+    gap = abs(f_gpu - f_ref) / abs(f_ref)
+    print(f"fp32 SGD baseline: last step errs {({k: f'{v:.1e}' for k, v in errs.items()})}, "
+          f"final loss gpu {f_gpu:.6f} sgd64 {f_ref:.6f} gap {gap:.2e}", flush=True)
+    assert f_gpu < math.log(2.0)
+    assert gap <= LOSS_GAP
+    h.close()

@@ -22,6 +22,7 @@ SMALL = {
     "logistic-4096x64": None,
     "epsilon": 20_000,
     "higgs": 200_000,
+    "susy": 200_000,
     "synth-lsq": 50_000,
     "poisson-synth": 50_000,
 }

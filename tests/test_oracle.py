@@ -510,3 +510,26 @@ def test_margin_choices_cover_float32_orders():
         for v32 in _f32_dot_orders(Y[i], w0, rng):
             got = float(torch.tensor([float(v32)], dtype=torch.float32).to(torch.bfloat16).to(torch.float64)[0])
             assert lo[i] <= got <= hi[i], (i, float(v32), lo[i], hi[i])
+
+
+@pytest.mark.parametrize("storage", ["bf16", "fp32"])
+def test_full_loss_across_its_row_chunks(storage):
+    """full_loss sums in chunks of 2^21 / n rows; m spans two whole chunks and
+    a ragged third.  Squared loss, w = e_0, y = 0: row i contributes
+    x_i0^2 / 2 with x_i0 = (i mod 16) / 16 (exact in bf16), so the mean has an
+    exact rational value; a dropped, repeated or shifted chunk changes it."""
+    n = 64
+    chunk = (1 << 21) // n
+    m = 2 * chunk + 37
+    X = np.zeros((m, n), np.float32)
+    X[:, 0] = (np.arange(m) % 16) / 16.0
+    X[:, 1:] = 3.0  # any other column is multiplied by w_j = 0
+    y = np.zeros(m, np.float32)
+    w = np.zeros(n)
+    w[0] = 1.0
+    exact = sum(Fraction(i % 16, 16) ** 2 / 2 for i in range(m)) / m
+    got = O.full_loss(X, y, w, "squared", storage=storage)
+    assert abs(got - float(exact)) <= 1e-15 * float(exact)
+    # the same rows with the last chunk's rows dropped would differ by more than rounding
+    short = sum(Fraction(i % 16, 16) ** 2 / 2 for i in range(2 * chunk)) / m
+    assert abs(float(short) - float(exact)) > 1e-6
