@@ -533,3 +533,153 @@ def test_full_loss_across_its_row_chunks(storage):
     # the same rows with the last chunk's rows dropped would differ by more than rounding
     short = sum(Fraction(i % 16, 16) ** 2 / 2 for i in range(2 * chunk)) / m
     assert abs(float(short) - float(exact)) > 1e-6
+
+
+# --------------------------------------------------------------------------
+# fp16 and fp8 storage, bf16-rounded Gram
+# --------------------------------------------------------------------------
+def _golden_rows(name):
+    rows = []
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            a, b, *_ = line.split()
+            rows.append((a, b))
+    return rows
+
+
+def _f32_of(hexbits):
+    return np.array([int(hexbits, 16)], dtype=np.uint32).view(np.float32)
+
+
+def test_f16_rounding_golden_cases():
+    for a, b in _golden_rows("fp16_rne_cases.txt"):
+        x = _f32_of(a)
+        assert int(O.f16_bits(x)[0]) == int(b, 16), (a, b, hex(int(O.f16_bits(x)[0])))
+        if not np.isnan(x[0]):
+            assert O.f16_to_f64(O.f16_bits(x))[0] == O.f16_round(x)[0] or np.isnan(O.f16_round(x)[0])
+
+
+def test_e4m3_rounding_golden_cases():
+    for a, b in _golden_rows("e4m3_rne_cases.txt"):
+        x = _f32_of(a)
+        assert int(O.e4m3_bits(x)[0]) == int(b, 16), (a, b, hex(int(O.e4m3_bits(x)[0])))
+
+
+def test_fp8_scale_exponent_golden_cases():
+    for a, b in _golden_rows("fp8_scale_cases.txt"):
+        x = float(_f32_of(a)[0])
+        k = O.fp8_exponent(x)
+        assert k == int(b), (a, b, k)
+        if x > 0:  # the defining property, checked exactly
+            assert x * 2.0 ** k <= 448.0 < x * 2.0 ** (k + 1)
+
+
+def _spread_f32(rng, count, lo_exp, hi_exp):
+    """float32 values over many binades, both signs, plus exact ties."""
+    mant = rng.uniform(1.0, 2.0, count)
+    ex = rng.integers(lo_exp, hi_exp, count)
+    x = (np.ldexp(mant, ex) * rng.choice([-1.0, 1.0], count)).astype(np.float32)
+    return x
+
+
+def test_f16_rounding_equals_numpy_conversion():
+    # NumPy converts float32 to float16 with round-to-nearest-even and
+    # overflow to infinity: the library routine the definition reduces to
+    rng = np.random.default_rng(71)
+    x = np.concatenate([_spread_f32(rng, 200000, -30, 18), np.float32([65504, 65519.996, 65520, 7e4])])
+    # ties: values exactly halfway between neighbouring fp16 values
+    h = rng.integers(1, 0x7BFF, 20000).astype(np.uint16).view(np.float16).astype(np.float64)
+    nxt = (rng.integers(1, 0x7BFF, 20000).astype(np.uint16)).view(np.float16).astype(np.float64)
+    x = np.concatenate([x, ((h + np.nextafter(h.astype(np.float16), np.float16(np.inf)).astype(np.float64)) / 2)
+                        .astype(np.float32), nxt.astype(np.float32)])
+    assert np.array_equal(O.f16_bits(x), x.astype(np.float16).view(np.uint16))
+
+
+def test_e4m3_rounding_equals_torch_conversion_in_range():
+    # torch's float8_e4m3fn conversion rounds to nearest even; it does not
+    # saturate, so the comparison stays at |x| <= 464 (the largest value that
+    # rounds to 448)
+    import torch
+    rng = np.random.default_rng(72)
+    x = _spread_f32(rng, 200000, -14, 9)
+    x = x[np.abs(x) <= 464.0]
+    ties = (O.e4m3_to_f64(np.arange(0, 0x7E, dtype=np.uint8)) + O.e4m3_to_f64(np.arange(1, 0x7F, dtype=np.uint8))) / 2
+    x = np.concatenate([x, ties.astype(np.float32), -ties.astype(np.float32)])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_bits(x), ref)
+
+
+@pytest.mark.parametrize("fmt,u,lo,hi", [("fp16", 2.0 ** -11, 2.0 ** -14, 65504.0),
+                                         ("e4m3", 2.0 ** -4, 2.0 ** -6, 448.0)])
+def test_rounding_error_within_unit_roundoff_and_monotone(fmt, u, lo, hi):
+    rng = np.random.default_rng(73)
+    x = np.sort(np.exp(rng.uniform(np.log(lo), np.log(hi), 100000))).astype(np.float32).astype(np.float64)
+    r = O.f16_round(x) if fmt == "fp16" else O.e4m3_round(x)
+    assert np.all(np.abs(r - x) <= u * np.abs(x))
+    assert np.all(np.diff(r) >= 0)
+    # decoding the bits gives the rounded value back
+    bits = O.f16_bits(x) if fmt == "fp16" else O.e4m3_bits(x)
+    dec = O.f16_to_f64(bits) if fmt == "fp16" else O.e4m3_to_f64(bits)
+    assert np.array_equal(dec, r)
+
+
+def test_fp8_stored_values_are_scaled_e4m3_values():
+    rng = np.random.default_rng(74)
+    X = (rng.standard_normal((50, 40)) * 0.03).astype(np.float32)
+    k = O.fp8_exponent_of(X)
+    assert np.max(np.abs(X)) * 2.0 ** k <= 448.0 < np.max(np.abs(X)) * 2.0 ** (k + 1)
+    V = O.stored_values(X, "fp8", k)
+    # every stored value times 2^k is an E4M3 value: its own rounding
+    assert np.array_equal(O.e4m3_round(np.ldexp(V, k)), np.ldexp(V, k))
+    # within half an E4M3 spacing of x: relative 2^-4 for entries past the subnormal range
+    big = np.abs(X) * 2.0 ** k >= 2.0 ** -6
+    assert np.all(np.abs(V - X)[big] <= 2.0 ** -4 * np.abs(X)[big])
+    with pytest.raises(ValueError):
+        O.stored_values(X, "fp8")
+
+
+def test_bf16_gram_rounds_float32_entries_once():
+    # G_{1,0} = y1 . y0 with y0 = e_0: 1 + 2^-8 is a bf16 tie (stays 1),
+    # 1 + 3 * 2^-8 a tie with an odd kept bit (rounds up to 1 + 2^-6)
+    for g, want in ((1.0 + 2.0 ** -8, 1.0), (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6), (3.0, 3.0)):
+        Y = np.array([[1.0, 0.0], [g, 5.0]])
+        G = O.gram_blocks(Y, 2, 1)
+        assert G[(1, 0)][0, 0] == g
+        assert O.stored_gram(G, "bf16")[(1, 0)][0, 0] == want
+        assert O.stored_gram(G, "fp32")[(1, 0)][0, 0] == g
+
+
+@pytest.mark.parametrize("loss", O.LOSSES)
+def test_bf16_gram_step_equals_fp32_step_when_entries_are_bf16_values(loss):
+    # small integer rows: every Gram entry is an integer below 256, a bf16
+    # value, so rounding G changes nothing
+    rng = np.random.default_rng(75)
+    s, b, n = 4, 3, 5
+    Y = rng.integers(-3, 4, (s * b, n)).astype(np.float64)
+    yB = np.abs(rng.integers(0, 3, s * b)).astype(np.float64) if loss == "poisson" else \
+        rng.choice([-1.0, 1.0], s * b)
+    w0 = rng.standard_normal(n) * 0.1
+    a = O.outer_step_rows(Y, yB, w0, s, b, 0.05, loss, gram="fp32")
+    c = O.outer_step_rows(Y, yB, w0, s, b, 0.05, loss, gram="bf16")
+    for key in ("z", "r", "w"):
+        assert np.array_equal(a[key], c[key])
+    # and a Gram that is not bf16-exact changes the step
+    Y2 = Y + 2.0 ** -9
+    a2 = O.outer_step_rows(Y2, yB, w0, s, b, 0.05, loss, gram="fp32")
+    c2 = O.outer_step_rows(Y2, yB, w0, s, b, 0.05, loss, gram="bf16")
+    assert not np.array_equal(a2["w"], c2["w"])
+
+
+def test_gram_choices_cover_float32_orders():
+    rng = np.random.default_rng(76)
+    s, b, n = 3, 8, 384
+    Y = O.stored_values((rng.standard_normal((s * b, n)) / np.sqrt(n)).astype(np.float32), "bf16")
+    near, lo, hi = O.gram_choices(Y, s, b)
+    for (j, t), g in near.items():
+        assert np.all((lo[(j, t)] <= g) & (g <= hi[(j, t)]))
+        for i in range(b):
+            for k in range(b):
+                for v32 in _f32_dot_orders(Y[j * b + i], Y[t * b + k], rng):
+                    r = O.stored_margins(np.array([float(v32)]), "bf16")[0]
+                    assert lo[(j, t)][i, k] <= r <= hi[(j, t)][i, k]
