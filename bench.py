@@ -169,7 +169,7 @@ def sgd_baselines(h_bf16, X, y, wl, steps: int, warmup: int, dev):
             torch.cuda.synchronize()
         ms = start.elapsed_time(stop)
         out[storage] = {"value": n_inner / (ms / 1e3), "unit": "inner SGD steps/s", "steps": n_inner,
-                        "us_per_step": ms * 1e3 / n_inner}
+                        "us_per_step": ms * 1e3 / n_inner, "final_loss": h.loss_value(w)}
         if h is not h_bf16:
             h.close()
             del h
@@ -307,6 +307,48 @@ def run_workload(wl, X, y, args, dev, detailed: bool):
     return res
 
 
+def precision_variants(h_main, X, y, wl, args, dev):
+    """The precision choices beyond the recipe, timed like the main run (K
+    steps after W warm-up steps, unstamped): fp16 and fp8 storage of X (their
+    rows go through the gather kernel each step) and G rounded once to bf16
+    (on the main handle).  Final loss of each, for the gap to float32 SGD."""
+    import torch
+    from communication_avoiding_mixed_amd import binding as B
+    K, W = args.steps, args.warmup
+    out = {}
+    stream = torch.cuda.Stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+
+    def timed(h):
+        w = torch.zeros(wl.n, device=dev)
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            h.train(wl.s, wl.b, wl.eta, 0, 0, W, w)
+            torch.cuda.synchronize()
+            start.record(stream)
+            h.train(wl.s, wl.b, wl.eta, 0, W, K, w)
+            stop.record(stream)
+            torch.cuda.synchronize()
+            loss = h.loss_value(w)
+        ms = start.elapsed_time(stop)
+        return {"value": wl.s * K / (ms / 1e3), "unit": "inner SGD steps/s", "ms_per_step": ms / K,
+                "final_loss": loss}
+
+    for storage in ("fp16", "fp8"):
+        h = B.CASGD(torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev), wl.loss, storage)
+        out[f"storage_{storage}"] = timed(h)
+        if storage == "fp8":
+            out["storage_fp8"]["scale_exponent"] = h.fp8_exponent
+        h.close()
+        torch.cuda.empty_cache()
+    h_main.set_option(B.OPT_GRAM_BF16, 1)
+    out["gram_bf16"] = timed(h_main)
+    out["gram_bf16"]["gram_bytes_packed"] = B.gram_bytes(wl.s, wl.b, packed=True) // 2
+    h_main.set_option(B.OPT_GRAM_BF16, 0)
+    return out
+
+
 def summarize(wl, r, K, peaks):
     """Throughput, roofline fractions and the per-kernel breakdown of one run."""
     alg = algorithmic(wl)
@@ -359,6 +401,8 @@ def main():
     ap.add_argument("--no-sgd-baseline", action="store_true",
                     help="skip the plain minibatch SGD runs (s = 1) of the same library")
     ap.add_argument("--no-peaks", action="store_true", help="skip the calibration kernels")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the fp16 / fp8 storage and bf16-Gram runs of the main workload")
     ap.add_argument("--layout", type=int, default=0, choices=(0, 1, 2, 3),
                     help="placement of the recurrence's workgroups (CASGD_OPT_CHAIN_LAYOUT): "
                          "0 automatic, 1 spread over the XCDs, 2 on one XCD, one per CU, "
@@ -397,6 +441,7 @@ def main():
     main_sum = summarize(wl, r, args.steps, peaks)
     print(f"[bench] {wl.name}: {main_sum['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
     sgd = None if args.no_sgd_baseline else sgd_baselines(r["h"], X, y, wl, args.steps, args.warmup, dev)
+    variants = None if args.no_variants else precision_variants(r["h"], X, y, wl, args, dev)
     r["h"].close()
     del r["h"]
     torch.cuda.empty_cache()
@@ -461,9 +506,15 @@ def main():
                         "ms_per_step": r["ms_mix"] / K, "final_loss": r["loss_mix"]},
         "workloads": workloads,
     }
+    if variants:
+        ref = sgd["fp32"]["final_loss"] if sgd else None
+        for v in variants.values():
+            v["gap_vs_fp32_sgd"] = abs(v["final_loss"] - ref) / abs(ref) if ref else None
+        out["precision_variants"] = variants
     if sgd:
         out["sgd_baseline"] = {"kind": "minibatch SGD, s = 1, same library and b, eta", **sgd}
         out["speedup_vs_fp32_sgd"] = main_sum["value"] / sgd["fp32"]["value"]
+        out["final_loss_gap_vs_fp32_sgd"] = abs(r["loss"] - sgd["fp32"]["final_loss"]) / abs(sgd["fp32"]["final_loss"])
         out["speedup_vs_bf16_sgd"] = main_sum["value"] / sgd["bf16"]["value"]
     if cpu:
         out["cpu_baseline"] = cpu

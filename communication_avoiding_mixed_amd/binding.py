@@ -17,18 +17,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcasgd.so")
 
 LOGISTIC, SQUARED, POISSON = 0, 1, 2
-BF16, FP32 = 0, 1
+BF16, FP32, FP16, FP8 = 0, 1, 2, 3
 OK, EINVAL, ENOMEM, EHIP = 0, -1, -2, -3
 EXPORT_IDX, EXPORT_Y, EXPORT_YB, EXPORT_G, EXPORT_V, EXPORT_Z, EXPORT_R = range(7)
 K_GATHER, K_GRAM, K_CHAIN, K_PIPE, K_TRAIN = range(5)
-OPT_RECURRENCE, OPT_SPIN_LIMIT, OPT_MARGIN_BF16, OPT_CHAIN_LAYOUT, OPT_TRAIN_FORM = 0, 1, 2, 3, 4
+OPT_RECURRENCE, OPT_SPIN_LIMIT, OPT_MARGIN_BF16, OPT_CHAIN_LAYOUT, OPT_TRAIN_FORM, OPT_GRAM_BF16 = 0, 1, 2, 3, 4, 5
 TRAIN_PERSISTENT, TRAIN_PER_STEP = 0, 1
 LAYOUT_AUTO, LAYOUT_SPREAD, LAYOUT_ONE_XCD = 0, 1, 2
 RECURRENCE_AUTO, RECURRENCE_ALL_TO_ALL, RECURRENCE_LOOKAHEAD = 0, 1, 2
 KERNEL_NAMES = {K_GATHER: "gather", K_GRAM: "gram", K_CHAIN: "chain", K_PIPE: "pipe", K_TRAIN: "train"}
 
 LOSS_IDS = {"logistic": LOGISTIC, "squared": SQUARED, "poisson": POISSON}
-STORAGE_IDS = {"bf16": BF16, "fp32": FP32}
+STORAGE_IDS = {"bf16": BF16, "fp32": FP32, "fp16": FP16, "fp8": FP8}
 
 # every entry point declared in include/casgd.h: name -> (restype, argtypes)
 _VP, _I64, _U64, _I, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int, ctypes.c_float
@@ -44,6 +44,7 @@ SIGNATURES = {
     "casgd_debug_export": (_I, [_VP, _I, _VP, ctypes.c_size_t]),
     "casgd_export_rows": (_I, [_VP, _I64, _I64, _VP, ctypes.c_size_t]),
     "casgd_ld": (_I64, [_VP]),
+    "casgd_fp8_exponent": (_I, [_VP]),
     "casgd_gram_bytes": (_I64, [_I, _I, _I]),
     "casgd_set_timing": (_I, [_VP, _I]),
     "casgd_get_timing": (_I, [_VP, _I, ctypes.POINTER(ctypes.c_double),
@@ -208,6 +209,11 @@ class CASGD:
         return float(out.value)
 
     # -- inspection
+    @property
+    def fp8_exponent(self) -> int:
+        """k of fp8 storage (X stored as E4M3 of x * 2^k); 0 otherwise."""
+        return int(load().casgd_fp8_exponent(self._handle()))
+
     def export(self, what: int) -> np.ndarray:
         if self._last is None:
             raise CasgdError("no outer step has run yet")
@@ -216,7 +222,8 @@ class CASGD:
         if what == EXPORT_IDX:
             arr = np.empty(sb, np.int32)
         elif what == EXPORT_Y:
-            arr = np.empty((sb, self.ld), np.uint16 if self.storage == "bf16" else np.float32)
+            # gathered rows: bf16 bits for bf16 and fp8 storage, fp16 bits, or float32
+            arr = np.empty((sb, self.ld), np.float32 if self.storage == "fp32" else np.uint16)
         elif what == EXPORT_G:
             arr = np.empty(b * b * s * (s - 1) // 2, np.float32)
         else:
@@ -226,7 +233,8 @@ class CASGD:
         return arr
 
     def export_rows(self, row0: int, nrows: int) -> np.ndarray:
-        arr = np.empty((nrows, self.ld), np.uint16 if self.storage == "bf16" else np.float32)
+        # stored rows: 16-bit patterns (bf16, fp16), E4M3 bytes (fp8) or float32
+        arr = np.empty((nrows, self.ld), {"fp32": np.float32, "fp8": np.uint8}.get(self.storage, np.uint16))
         _check(load().casgd_export_rows(self._handle(), row0, nrows,
                                         arr.ctypes.data_as(ctypes.c_void_p), arr.nbytes),
                "casgd_export_rows")

@@ -30,6 +30,8 @@
 // process ends; every call on that GPU shares it.  Host code never uses this
 // name as an address: the device address comes from hipGetSymbolAddress.
 constexpr int kNoAllocPartials = casgd::kLossBlocks;
+// casgd_create finds fp8's max |x| in the loss buffers
+static_assert(sizeof(double) * casgd::kLossBlocks >= sizeof(uint32_t) * casgd::kMaxAbsBlocks, "max-abs partials");
 static __device__ __align__(256) double scratch[kNoAllocPartials];
 
 namespace {
@@ -88,7 +90,10 @@ struct StepBuffers {
 struct casgd_ctx {
   int64_t m = 0, n = 0, ld = 0;
   int loss = 0, storage = 0;
-  size_t esize = 0;
+  size_t esize = 0;  // bytes of a stored element
+  size_t ysize = 0;  // bytes of an element of the gathered rows Y (row_kind)
+  int fp8_exp = 0;   // fp8 storage: X is stored as e4m3(x * 2^fp8_exp)
+  int gram_bf16 = 0; // CASGD_OPT_GRAM_BF16
   void* Xs = nullptr;
   float* y = nullptr;
   hipStream_t stream = nullptr;  // caller's stream: weight-dependent work
@@ -191,7 +196,7 @@ int ensure_workspace(casgd_ctx* h, int s, int b) {
   free_workspace(h);
   bool ok = true;
   for (auto& bset : h->buf) {
-    ok = ok && grab(bset.idx, sizeof(int32_t) * new_sb) && grab(bset.Y, h->esize * h->ld * new_sb) &&
+    ok = ok && grab(bset.idx, sizeof(int32_t) * new_sb) && grab(bset.Y, h->ysize * h->ld * new_sb) &&
          grab(bset.yB, sizeof(float) * new_sb) && grab(bset.G, sizeof(float) * new_g);
   }
   ok = ok && grab(h->v, sizeof(float) * new_sb) && grab(h->z, sizeof(float) * new_sb) &&
@@ -310,12 +315,13 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
   if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   e = timed(h, CASGD_K_GATHER, [&](const casgd::LaunchTimer& tm) {
     return casgd::launch_gather(h->storage, h->Xs, h->y, h->m, h->ld, sb, seed, idx_in, B.idx,
-                                B.Y, B.yB, h->prep, tm);
+                                B.Y, B.yB, h->fp8_exp, h->prep, tm);
   });
   if (e != hipSuccess) return hip_fail(e, "gather launch");
   const casgd::GramPlan plan = casgd::gram_plan(h->storage, s, b, h->ld);
   e = timed(h, CASGD_K_GRAM, [&](const casgd::LaunchTimer& tm) {
-    return casgd::launch_gram(h->storage, B.Y, h->ld, s, b, B.G, plan, h->order[0], h->prep, tm);
+    return casgd::launch_gram(casgd::row_kind(h->storage), B.Y, h->ld, s, b, B.G, plan, h->order[0],
+                              h->gram_bf16, h->prep, tm);
   });
   if (e != hipSuccess) return hip_fail(e, "gram launch");
   e = hipEventRecord(h->ev_prep[k], h->prep);
@@ -368,12 +374,12 @@ int run_outer(casgd_ctx* h, int s, int b, float eta, uint64_t seed, const int32_
     p.mar_rows = kMarginRows;
     p.mar_wgs = (sb + kMarginRows - 1) / kMarginRows;
     e = timed(h, CASGD_K_CHAIN, [&](const casgd::LaunchTimer& tm) {
-      return casgd::launch_step(h->storage, h->loss, p, h->stream, tm);
+      return casgd::launch_step(casgd::row_kind(h->storage), h->loss, p, h->stream, tm);
     });
   } else {
     e = timed(h, CASGD_K_CHAIN, [&](const casgd::LaunchTimer& tm) {
-      return la.ok ? casgd::launch_chain_la(h->storage, h->loss, a, la, h->stream, tm)
-                   : casgd::launch_chain(h->storage, h->loss, a, h->stream, tm);
+      return la.ok ? casgd::launch_chain_la(casgd::row_kind(h->storage), h->loss, a, la, h->stream, tm)
+                   : casgd::launch_chain(casgd::row_kind(h->storage), h->loss, a, h->stream, tm);
     });
   }
   if (e != hipSuccess) return launch_fail(e, "recurrence launch");
@@ -448,6 +454,7 @@ int run_train_persist(casgd_ctx* h, const casgd::ChainPlan& cp, int s, int b, fl
   A.stride = cp.stride;
   A.loss = h->loss;
   A.vround = h->margin_bf16;
+  A.gbf16 = h->gram_bf16;
   A.c = eta / static_cast<float>(b);
   A.n_outer = n;
   A.base_seed = base_seed;
@@ -490,7 +497,7 @@ int run_train_persist(casgd_ctx* h, const casgd::ChainPlan& cp, int s, int b, fl
   StepBuffers& B = h->buf[(n - 1) % 3];
   e = casgd::launch_gather(h->storage, h->Xs, h->y, h->m, h->ld, sb,
                            casgd::splitmix64(base_seed, first + static_cast<uint64_t>(n - 1)), nullptr, B.idx, B.Y,
-                           B.yB, h->stream);
+                           B.yB, h->fp8_exp, h->stream);
   if (e != hipSuccess) return hip_fail(e, "gather of the last step");
   e = hipEventRecord(h->ev_chain[0], h->stream);
   if (e == hipSuccess) e = hipEventRecord(h->ev_chain[1], h->stream);
@@ -532,7 +539,7 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
     StepBuffers& A = h->buf[i % 3];
     return timed(h, CASGD_K_GATHER, [&](const casgd::LaunchTimer& tm) {
       return casgd::launch_gather(h->storage, h->Xs, h->y, h->m, h->ld, sb, seed_of(i), nullptr, A.idx,
-                                  A.Y, A.yB, h->stream, tm);
+                                  A.Y, A.yB, h->fp8_exp, h->stream, tm);
     });
   };
   const casgd::GramPlan plan = casgd::gram_plan(h->storage, s, b, h->ld);
@@ -540,8 +547,8 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
   e = gather(0);
   if (e == hipSuccess)
     e = timed(h, CASGD_K_GRAM, [&](const casgd::LaunchTimer& tm) {
-      return casgd::launch_gram(h->storage, h->buf[0].Y, h->ld, s, b, h->buf[0].G, plan, h->order[0],
-                                h->stream, tm);
+      return casgd::launch_gram(casgd::row_kind(h->storage), h->buf[0].Y, h->ld, s, b, h->buf[0].G, plan,
+                                h->order[0], h->gram_bf16, h->stream, tm);
     });
   if (e == hipSuccess && n > 1) e = gather(1);
   if (e != hipSuccess) return hip_fail(e, "pipeline prologue");
@@ -687,7 +694,7 @@ casgd_handle casgd_create(const float* X, const float* y, int64_t m, int64_t n, 
     fail(CASGD_EINVAL, "unknown loss");
     return nullptr;
   }
-  if (storage != CASGD_BF16 && storage != CASGD_FP32) {
+  if (storage != CASGD_BF16 && storage != CASGD_FP32 && storage != CASGD_FP16 && storage != CASGD_FP8) {
     fail(CASGD_EINVAL, "unknown storage type");
     return nullptr;
   }
@@ -697,7 +704,8 @@ casgd_handle casgd_create(const float* X, const float* y, int64_t m, int64_t n, 
   h->ld = (n + 31) / 32 * 32;
   h->loss = loss;
   h->storage = storage;
-  h->esize = storage == CASGD_BF16 ? 2 : 4;
+  h->esize = casgd::elem_bytes(storage);
+  h->ysize = casgd::elem_bytes(casgd::row_kind(storage));
   bool ok = hipStreamCreateWithFlags(&h->prep, hipStreamNonBlocking) == hipSuccess &&
             hipEventCreateWithFlags(&h->ev_switch, hipEventDisableTiming) == hipSuccess;
   for (int i = 0; i < 2 && ok; ++i)
@@ -737,7 +745,23 @@ casgd_handle casgd_create(const float* X, const float* y, int64_t m, int64_t n, 
     e = hipMemsetAsync(h->place, 0, sizeof(unsigned long long) * casgd::kChainMaxWorkgroups, h->stream);
   if (e == hipSuccess) e = hipMemsetAsync(h->prog, 0, sizeof(unsigned long long) * kProgWords, h->stream);
   if (e == hipSuccess) e = hipMemsetAsync(h->wbox, 0, sizeof(unsigned long long) * n, h->stream);
-  if (e == hipSuccess) e = casgd::launch_store(storage, X, h->Xs, m, n, h->ld, h->stream);
+  if (e == hipSuccess && storage == CASGD_FP8) {
+    // the scale exponent: the largest k with max|x| * 2^k <= 448 = 0.875 * 2^9
+    uint32_t bits = 0;
+    e = casgd::launch_maxabs(X, m * n, reinterpret_cast<uint32_t*>(h->loss_partial),
+                             reinterpret_cast<uint32_t*>(h->loss_out), h->stream);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(&bits, h->loss_out, sizeof(bits), hipMemcpyDeviceToHost, h->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+    float mx = 0.f;
+    std::memcpy(&mx, &bits, sizeof(mx));
+    if (std::isfinite(mx) && mx > 0.f) {
+      int E = 0;
+      const double f = std::frexp(static_cast<double>(mx), &E);
+      h->fp8_exp = f <= 0.875 ? 9 - E : 8 - E;
+    }
+  }
+  if (e == hipSuccess) e = casgd::launch_store(storage, X, h->Xs, m, n, h->ld, h->fp8_exp, h->stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(h->y, y, sizeof(float) * m, hipMemcpyDeviceToDevice, h->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
@@ -792,6 +816,8 @@ int casgd_set_stream(casgd_handle h, void* stream) {
 
 int64_t casgd_ld(casgd_handle h) { return h ? h->ld : -1; }
 
+int casgd_fp8_exponent(casgd_handle h) { return h ? h->fp8_exp : 0; }
+
 int casgd_set_option(casgd_handle h, int option, int value) {
   if (!h) return fail(CASGD_EINVAL, "NULL handle");
   if (option == CASGD_OPT_RECURRENCE && value >= 0 && value <= 2) {
@@ -808,6 +834,10 @@ int casgd_set_option(casgd_handle h, int option, int value) {
   }
   if (option == CASGD_OPT_CHAIN_LAYOUT && value >= 0 && value <= 3) {
     h->layout = value;
+    return CASGD_OK;
+  }
+  if (option == CASGD_OPT_GRAM_BF16 && (value == 0 || value == 1)) {
+    h->gram_bf16 = value;
     return CASGD_OK;
   }
   if (option == CASGD_OPT_TRAIN_FORM && (value == 0 || value == 1)) {
@@ -851,7 +881,10 @@ int casgd_train(casgd_handle h, int s, int b, float eta, uint64_t base_seed, uin
   int rc = check_step_args(h, s, b, w);
   if (rc != CASGD_OK) return rc;
   if (n_outer < 0) return fail(CASGD_EINVAL, "n_outer must be >= 0");
-  if (n_outer > 0 && h->recurrence != 2) {
+  // the pipelined and persistent launches read stored rows themselves: bf16
+  // and float32 storage; fp16 and fp8 rows go through the gather each step
+  const bool fused = h->storage == CASGD_BF16 || h->storage == CASGD_FP32;
+  if (n_outer > 0 && h->recurrence != 2 && fused) {
     const casgd::ChainPlan cp = plan_chain(h, s, b);
     if (cp.lean && h->train_form == 0 && persist_margin_rows(h, cp, s, b) > 0)
       return run_train_persist(h, cp, s, b, eta, base_seed, first_step, n_outer, w);
@@ -868,7 +901,7 @@ int casgd_loss(casgd_handle h, const float* w, double* out) {
   if (!h) return fail(CASGD_EINVAL, "NULL handle");
   if (!w || !out) return fail(CASGD_EINVAL, "NULL pointer");
   hipError_t e = casgd::launch_loss(h->storage, h->loss, h->Xs, h->y, h->m, h->n, h->ld, w,
-                                    h->loss_partial, h->loss_out, h->stream);
+                                    h->loss_partial, h->loss_out, h->fp8_exp, h->stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(out, h->loss_out, sizeof(double), hipMemcpyDeviceToHost, h->stream);
   if (e == hipSuccess) e = sync_all(h);
@@ -885,7 +918,7 @@ int casgd_loss_noalloc(casgd_handle h, const float* w, double* out_dev) {
     return fail(CASGD_EINVAL, "the loss needs " + std::to_string(np) + " partial sums; the static scratch holds " +
                                   std::to_string(kNoAllocPartials));
   const hipError_t e = casgd::launch_loss(h->storage, h->loss, h->Xs, h->y, h->m, h->n, h->ld, w, h->scratch,
-                                          out_dev, h->stream);
+                                          out_dev, h->fp8_exp, h->stream);
   if (e != hipSuccess) return hip_fail(e, "loss launch");
   return CASGD_OK;
 }
@@ -901,7 +934,7 @@ int casgd_debug_export(casgd_handle h, int what, void* dst, size_t bytes) {
   size_t need = 0;
   switch (what) {
     case CASGD_EXPORT_IDX: src = B.idx; need = sb * sizeof(int32_t); break;
-    case CASGD_EXPORT_Y: src = B.Y; need = sb * h->ld * h->esize; break;
+    case CASGD_EXPORT_Y: src = B.Y; need = sb * h->ld * h->ysize; break;
     case CASGD_EXPORT_YB: src = B.yB; need = sb * sizeof(float); break;
     case CASGD_EXPORT_G:
       src = B.G;

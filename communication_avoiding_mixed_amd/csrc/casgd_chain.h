@@ -31,6 +31,18 @@ struct Elems<uint16_t> {
   }
 };
 template <>
+struct Elems<_Float16> {
+  static constexpr int E = 8;
+  __device__ static void widen(const u32x4& q, float (&f)[8]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = f16_to_f32(w[e] & 0xFFFFu);
+      f[2 * e + 1] = f16_to_f32(w[e] >> 16);
+    }
+  }
+};
+template <>
 struct Elems<float> {
   static constexpr int E = 4;
   __device__ static void widen(const u32x4& q, float (&f)[4]) {

@@ -45,6 +45,85 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+// Round-to-nearest-even of a float32 magnitude (bit pattern a, below the
+// target format's smallest normal) to a count of the target's subnormal
+// quanta 2^qexp: a = mant * 2^(e - 150) with the implicit bit, so the count is
+// mant * 2^(e - 150 - qexp), a right shift by sh = 150 + qexp - e (at least
+// 14 here).  Host and device share these conversions.
+__host__ __device__ __forceinline__ uint32_t subnormal_quanta(uint32_t a, int qexp) {
+  const int e = static_cast<int>(a >> 23);
+  const int sh = 150 + qexp - e;
+  if (e == 0 || sh > 24) return 0u;  // below half a quantum (or a float32 subnormal)
+  const uint32_t mant = (a & 0x7FFFFFu) | 0x800000u;
+  const uint32_t q = mant >> sh;
+  const uint32_t rem = mant & ((1u << sh) - 1u);
+  const uint32_t half = 1u << (sh - 1);
+  return q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
+}
+
+// float32 -> IEEE binary16 bits: round to nearest even, subnormals kept,
+// overflow (|x| >= 65520 after rounding, infinities) to infinity, NaN -> quiet
+// NaN with the sign kept.
+__host__ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return static_cast<uint16_t>(sign | 0x7E00u);
+  if (a >= 0x477FF000u) return static_cast<uint16_t>(sign | 0x7C00u);  // 65520: rounds past 65504
+  if (a >= 0x38800000u) {                                              // 2^-14: a binary16 normal
+    uint32_t r = a - (112u << 23);                                     // rebias 127 -> 15
+    r += 0xFFFu + ((r >> 13) & 1u);                                    // 13 dropped fraction bits
+    return static_cast<uint16_t>(sign | (r >> 13));
+  }
+  return static_cast<uint16_t>(sign | subnormal_quanta(a, -24));  // 1024 quanta is 2^-14, bits 0x400
+}
+
+// Exact float32 value of binary16 bits.
+__host__ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  const uint32_t sign = (h & 0x8000u) << 16;
+  const uint32_t e = (h >> 10) & 0x1Fu, f = h & 0x3FFu;
+  uint32_t bits;
+  if (e == 0)
+    bits = sign | __builtin_bit_cast(uint32_t, static_cast<float>(f) * 0x1p-24f);
+  else if (e == 31)
+    bits = sign | 0x7F800000u | (f << 13);
+  else
+    bits = sign | ((e + 112u) << 23) | (f << 13);
+  return __builtin_bit_cast(float, bits);
+}
+
+// float32 -> OCP E4M3 bits: round to nearest even, subnormals (quanta of
+// 2^-9) kept, magnitudes from 448 up (and infinities) saturated to 448, NaN
+// -> 0x7F with the sign kept.  Magnitudes in (448, 464] round to 448 and
+// larger ones would round past it, so every a >= 448 gives 448.
+__host__ __device__ __forceinline__ uint8_t f32_to_e4m3(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return static_cast<uint8_t>(sign | 0x7Fu);
+  if (a >= 0x43E00000u) return static_cast<uint8_t>(sign | 0x7Eu);
+  if (a >= 0x3C800000u) {             // 2^-6: an E4M3 normal
+    uint32_t r = a - (120u << 23);     // rebias 127 -> 7
+    r += 0x7FFFFu + ((r >> 20) & 1u);  // 20 dropped fraction bits
+    return static_cast<uint8_t>(sign | (r >> 20));
+  }
+  return static_cast<uint8_t>(sign | subnormal_quanta(a, -9));  // 8 quanta is 2^-6, bits 0x08
+}
+
+// Exact float32 value of E4M3 bits (0x7F / 0xFF are NaN).
+__host__ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t sign = (b & 0x80u) << 24;
+  const uint32_t e = (b >> 3) & 0xFu, f = b & 7u;
+  uint32_t bits;
+  if (e == 0)
+    bits = sign | __builtin_bit_cast(uint32_t, static_cast<float>(f) * 0x1p-9f);
+  else if (e == 15 && f == 7)
+    bits = sign | 0x7FC00000u;
+  else
+    bits = sign | ((e + 120u) << 23) | (f << 20);
+  return __builtin_bit_cast(float, bits);
+}
+
 // Derivative of the per-row loss with respect to the margin z, in float32.
 //   logistic: -y * sigmoid(-y z) (exp of a non-positive argument only)
 //   squared:  z - y

@@ -1,6 +1,7 @@
 // One 64 x 64 output tile of the strictly-lower block triangle of G = Y Y^T,
 // on bf16 MFMA (v_mfma_f32_32x32x16_bf16, float32 accumulators) for bf16
-// storage or on the vector ALUs for float32 storage, as device functions so
+// rows, on fp16 MFMA (v_mfma_f32_32x32x16_f16, the same operand layout) for
+// fp16 rows, or on the vector ALUs for float32 rows, as device functions so
 // both the stand-alone Gram kernel and the pipelined step kernel run the same
 // code.  The Abstract of "Mixed-Precision Communication-Avoiding
 // SGD for Generalized Linear Models on GPUs" forms the Gram from low-precision
@@ -16,6 +17,7 @@ namespace casgd {
 namespace gram {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 64;  // output tile edge; 4 waves of 32 x 32
@@ -44,17 +46,22 @@ struct SameRow {
   __device__ int64_t operator()(int r) const { return r; }
 };
 
+// gr: G communicated in low precision, each float32 entry rounded once to
+// the nearest bf16 (ties to even) as it is stored.
 template <bool WT>
-__device__ __forceinline__ void store_g(float* p, float v) {
+__device__ __forceinline__ void store_g(float* p, float v, bool gr) {
+  if (gr) v = bf16_to_f32(f32_to_bf16(v));
   if constexpr (WT)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else
     *p = v;
 }
 
-template <int BK, int D, bool WT = false, typename RowOf = SameRow>
+// F16: the 16-bit rows are fp16 (else bf16).
+template <int BK, int D, bool WT = false, typename RowOf = SameRow, bool F16 = false>
 __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ Y, int64_t ld, int b, int tps,
-                                          float* __restrict__ G, int tile, uint16_t* lds, RowOf row_of = {}) {
+                                          float* __restrict__ G, int tile, uint16_t* lds, RowOf row_of = {},
+                                          bool gr = false) {
   constexpr int CPR = BK / 8;          // 16-byte chunks per tile row per stage
   constexpr int RPP = 256 / CPR;       // tile rows loaded per pass
   constexpr int PASSES = kTile / RPP;  // passes per operand per stage
@@ -143,9 +150,15 @@ __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ Y, int64_
       load_stage(d, st0 + d + D);
 #pragma unroll
       for (int kk = 0; kk < NACC; ++kk) {
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&As[buf * BUF + arow * LW + kk * 16 + kofs]);
-        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&Bs[buf * BUF + brow * LW + kk * 16 + kofs]);
-        acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[kk], 0, 0, 0);
+        if constexpr (F16) {
+          const f16x8_t av = *reinterpret_cast<const f16x8_t*>(&As[buf * BUF + arow * LW + kk * 16 + kofs]);
+          const f16x8_t bv = *reinterpret_cast<const f16x8_t*>(&Bs[buf * BUF + brow * LW + kk * 16 + kofs]);
+          acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[kk], 0, 0, 0);
+        } else {
+          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&As[buf * BUF + arow * LW + kk * 16 + kofs]);
+          const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&Bs[buf * BUF + brow * LW + kk * 16 + kofs]);
+          acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[kk], 0, 0, 0);
+        }
       }
     }
   }
@@ -162,7 +175,7 @@ __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ Y, int64_
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int row = a0 + wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (row < b) store_g<WT>(&gcol[row * ldg], acc[0][e]);
+      if (row < b) store_g<WT>(&gcol[row * ldg], acc[0][e], gr);
     }
   }
 }
@@ -175,7 +188,8 @@ constexpr int kF32LdsElems = 2 * kF32BK * (kTile + 4);
 
 template <bool WT = false, typename RowOf = SameRow>
 __device__ __forceinline__ void f32_tile(const float* __restrict__ Y, int64_t ld, int b, int tps,
-                                         float* __restrict__ G, int tile, float* lds, RowOf row_of = {}) {
+                                         float* __restrict__ G, int tile, float* lds, RowOf row_of = {},
+                                         bool gr = false) {
   constexpr int BK = kF32BK;
   constexpr int LW = kTile + 4;
   float* As = lds;            // [BK][LW]
@@ -233,7 +247,7 @@ __device__ __forceinline__ void f32_tile(const float* __restrict__ Y, int64_t ld
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int col = b0 + tx * 4 + q;
-      if (col < b) store_g<WT>(&Gj[row * ldg + static_cast<int64_t>(t) * b + col], acc[u][q]);
+      if (col < b) store_g<WT>(&Gj[row * ldg + static_cast<int64_t>(t) * b + col], acc[u][q], gr);
     }
   }
 }

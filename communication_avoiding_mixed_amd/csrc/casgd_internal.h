@@ -32,15 +32,30 @@ hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, size_
 
 constexpr int kStoreBF16 = 0;
 constexpr int kStoreF32 = 1;
+constexpr int kStoreF16 = 2;
+constexpr int kStoreF8 = 3;  // OCP E4M3 of X * 2^k, k one exponent per matrix
 
-// X (float32 m x n) -> stored rows (m x ld, zero-padded), bf16 or f32.
+// Element type of the gathered rows Y, which the Gram, the margins, the
+// recurrence and the update read: the storage type, except that fp8 rows
+// are widened (exactly) to bf16 by the gather.
+inline int row_kind(int storage) { return storage == kStoreF8 ? kStoreBF16 : storage; }
+inline int elem_bytes(int kind) { return kind == kStoreF32 ? 4 : kind == kStoreF8 ? 1 : 2; }
+
+// X (float32 m x n) -> stored rows (m x ld, zero-padded) of the storage type;
+// fp8 stores e4m3(x * 2^fp8_exp).
 hipError_t launch_store(int storage, const float* X, void* Xs, int64_t m, int64_t n,
-                        int64_t ld, hipStream_t stream);
+                        int64_t ld, int fp8_exp, hipStream_t stream);
+// Largest |x| over count floats as a float32 bit pattern into *out_dev (a
+// NaN above every number); partial holds kMaxAbsBlocks words.
+constexpr int kMaxAbsBlocks = 1024;
+hipError_t launch_maxabs(const float* X, int64_t count, uint32_t* partial, uint32_t* out_dev,
+                         hipStream_t stream);
 
-// Sample (or take idx_in), gather rows into Y and labels into yB.
+// Sample (or take idx_in), gather rows into Y (of row_kind(storage)) and
+// labels into yB; fp8 rows are divided by 2^fp8_exp as they are widened.
 hipError_t launch_gather(int storage, const void* Xs, const float* y, int64_t m, int64_t ld,
                          int sb, uint64_t seed, const int32_t* idx_in, int32_t* idx_out,
-                         void* Y, float* yB, hipStream_t stream, const LaunchTimer& tm = {});
+                         void* Y, float* yB, int fp8_exp, hipStream_t stream, const LaunchTimer& tm = {});
 
 // Strictly-lower block triangle of Y Y^T in block-row layout, one 64 x 64
 // output tile per workgroup.
@@ -62,8 +77,9 @@ inline int gram_variant(int64_t ld) {
   return nstage >= 8 ? 1 : nstage >= 4 ? 2 : 3;
 }
 std::vector<int> gram_order(int s, int b, int nx = kXcds);
-hipError_t launch_gram(int storage, const void* Y, int64_t ld, int s, int b, float* G,
-                       const GramPlan& plan, const int* order, hipStream_t stream,
+// kind: row_kind of the storage; gr: round each entry of G once to bf16.
+hipError_t launch_gram(int kind, const void* Y, int64_t ld, int s, int b, float* G,
+                       const GramPlan& plan, const int* order, int gr, hipStream_t stream,
                        const LaunchTimer& tm = {});
 
 // Margins, inner recurrence and update in one launch of Q workgroups.
@@ -143,6 +159,7 @@ struct PipeArgs {
   const void* gY = nullptr;  // Y of step k+1 (stored type)
   float* gG = nullptr;           // G of step k+1
   const int* order = nullptr;
+  int gbf16 = 0;  // the Gram role rounds each entry of G once to bf16
   int gath0 = 0, gath_wgs = 0, gs = 0;  // gs: lanes per row (gather::group_size)
   const void* Xs = nullptr;
   const float* y = nullptr;
@@ -192,7 +209,7 @@ hipError_t launch_chain_la(int storage, int loss, const ChainArgs& a, const LaPl
 constexpr int kLossBlocks = 2048;
 hipError_t launch_loss(int storage, int loss, const void* Xs, const float* y, int64_t m,
                        int64_t n, int64_t ld, const float* w, double* partial, double* out_dev,
-                       hipStream_t stream);
+                       int fp8_exp, hipStream_t stream);
 // The partial sums launch_loss writes for this shape (at most kLossBlocks).
 int loss_partials(int storage, int64_t m, int64_t ld);
 

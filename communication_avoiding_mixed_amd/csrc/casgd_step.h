@@ -624,8 +624,9 @@ __device__ __forceinline__ void gather_rows(const PipeArgs& p, int g) {
                          row0 + static_cast<int>(threadIdx.x) / GS, threadIdx.x % GS);
 }
 
-// T = uint16_t: bf16 storage, Gram on MFMA with (BK, D) stages; T = float:
-// float32 storage, Gram on the vector ALUs (BK, D unused).
+// T = uint16_t: bf16 rows, Gram on MFMA with (BK, D) stages; T = _Float16:
+// fp16 rows (margins and recurrence only: no Gram role); T = float: float32
+// rows, Gram on the vector ALUs (BK, D unused).
 template <typename T, int NO, int CP, int BK, int D>
 __global__ __launch_bounds__(kThreads) void step_kernel(PipeArgs p, int loss) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
@@ -654,10 +655,11 @@ __global__ __launch_bounds__(kThreads) void step_kernel(PipeArgs p, int loss) {
     const int tile = p.order[w - p.gram0];
     if (tile >= 0) {
       if constexpr (std::is_same<T, float>::value)
-        gram::f32_tile(static_cast<const float*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile, sm);
-      else
+        gram::f32_tile(static_cast<const float*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile, sm, gram::SameRow{},
+                       p.gbf16 != 0);
+      else if constexpr (std::is_same<T, uint16_t>::value)
         gram::bf16_tile<BK, D>(static_cast<const uint16_t*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile,
-                               reinterpret_cast<uint16_t*>(sm));
+                               reinterpret_cast<uint16_t*>(sm), gram::SameRow{}, p.gbf16 != 0);
     }
     return;
   }
@@ -704,7 +706,11 @@ hipError_t launch_t(const PipeArgs& p, int loss, int grid, size_t lds, hipStream
 template <int NO, int CP>
 hipError_t launch_variant(int storage, int loss, const PipeArgs& p, int grid, size_t lds, hipStream_t st,
                           const LaunchTimer& tm) {
-  if (storage != kStoreBF16) return launch_t<float, NO, CP, 0, 0>(p, loss, grid, lds, st, tm);
+  if (storage == kStoreF32) return launch_t<float, NO, CP, 0, 0>(p, loss, grid, lds, st, tm);
+  if (storage == kStoreF16) {
+    if (p.gram_slots > 0) return hipErrorInvalidValue;  // fp16 rows: no Gram role here
+    return launch_t<_Float16, NO, CP, 0, 0>(p, loss, grid, lds, st, tm);
+  }
   switch (gram_variant(p.a.ld)) {
     case 0: return launch_t<uint16_t, NO, CP, 32, 1>(p, loss, grid, lds, st, tm);
     case 1: return launch_t<uint16_t, NO, CP, 64, 8>(p, loss, grid, lds, st, tm);

@@ -47,6 +47,7 @@ struct TrainArgs {
   const float* y;        // labels / targets, m
   int64_t m, n, ld;
   int s, b, Q, stride, loss, vround;
+  int gbf16;             // the Gram role rounds each entry of G once to bf16
   float c;
   int n_outer;
   uint64_t base_seed, first;  // step k samples with splitmix64(base_seed, first + k)
@@ -432,10 +433,11 @@ __device__ __forceinline__ void gram_role(const TrainArgs& A, int gw) {
       const int tile = A.order[p];
       if (tile < 0) continue;
       if constexpr (std::is_same<T, float>::value)
-        gram::f32_tile<true>(static_cast<const float*>(A.Xs), A.ld, A.b, A.tps, A.G[k % kRing], tile, sm, row_of);
+        gram::f32_tile<true>(static_cast<const float*>(A.Xs), A.ld, A.b, A.tps, A.G[k % kRing], tile, sm, row_of,
+                             A.gbf16 != 0);
       else
         gram::bf16_tile<BK, D, true>(static_cast<const uint16_t*>(A.Xs), A.ld, A.b, A.tps, A.G[k % kRing], tile,
-                                     reinterpret_cast<uint16_t*>(sm), row_of);
+                                     reinterpret_cast<uint16_t*>(sm), row_of, A.gbf16 != 0);
       __syncthreads();  // the tile's LDS is reused by the next one
     }
     __builtin_amdgcn_s_waitcnt(0);  // this workgroup's G stores written through
@@ -490,7 +492,8 @@ hipError_t launch_t(const TrainArgs& A, int grid, size_t lds, hipStream_t st, co
 template <int NO, int CP>
 hipError_t launch_variant(int storage, const TrainArgs& A, int grid, size_t lds, hipStream_t st,
                           const LaunchTimer& tm) {
-  if (storage != kStoreBF16) return launch_t<float, NO, CP, 0, 0>(A, grid, lds, st, tm);
+  if (storage == kStoreF32) return launch_t<float, NO, CP, 0, 0>(A, grid, lds, st, tm);
+  if (storage != kStoreBF16) return hipErrorInvalidValue;  // reads stored rows: bf16 and float32 storage only
   switch (gram_variant(A.ld)) {
     case 0: return launch_t<uint16_t, NO, CP, 32, 1>(A, grid, lds, st, tm);
     case 1: return launch_t<uint16_t, NO, CP, 64, 8>(A, grid, lds, st, tm);

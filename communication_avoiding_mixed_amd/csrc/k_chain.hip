@@ -742,10 +742,12 @@ __global__ __launch_bounds__(kThreads) void pipe_kernel(PipeArgs p) {
     const int tile = p.order[w - p.gram0];
     if (tile >= 0) {
       if constexpr (std::is_same<T, float>::value)
-        gram::f32_tile(static_cast<const float*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile, sm);
+        gram::f32_tile(static_cast<const float*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile, sm, gram::SameRow{},
+                       p.gbf16 != 0);
       else
-        gram::bf16_tile<BK, D>(static_cast<const uint16_t*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile,
-                               reinterpret_cast<uint16_t*>(sm));
+        gram::bf16_tile<BK, D, false, gram::SameRow, std::is_same<T, _Float16>::value>(
+            static_cast<const uint16_t*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile, reinterpret_cast<uint16_t*>(sm),
+            gram::SameRow{}, p.gbf16 != 0);
     }
     return;
   }
@@ -884,12 +886,18 @@ hipError_t launch_chain(int storage, int loss, const ChainArgs& a_in, hipStream_
     if (loss == kSquared) return chain_t<uint16_t, kSquared>(a, lds, st, tm);
     return chain_t<uint16_t, kPoisson>(a, lds, st, tm);
   }
+  if (storage == kStoreF16) {
+    if (loss == kLogistic) return chain_t<_Float16, kLogistic>(a, lds, st, tm);
+    if (loss == kSquared) return chain_t<_Float16, kSquared>(a, lds, st, tm);
+    return chain_t<_Float16, kPoisson>(a, lds, st, tm);
+  }
   if (loss == kLogistic) return chain_t<float, kLogistic>(a, lds, st, tm);
   if (loss == kSquared) return chain_t<float, kSquared>(a, lds, st, tm);
   return chain_t<float, kPoisson>(a, lds, st, tm);
 }
 
 hipError_t launch_pipe(int storage, int loss, const PipeArgs& p_in, hipStream_t st, const LaunchTimer& tm) {
+  if (storage != kStoreBF16 && storage != kStoreF32) return hipErrorInvalidValue;  // bf16 and float32 rows only
   PipeArgs p = p_in;
   p.a.preload = chain_preload(p.a.s, p.a.b, p.a.Q, p.a.ld) ? 1 : 0;
   // Spread chain workgroups share XCDs with the other roles: whole-CU LDS

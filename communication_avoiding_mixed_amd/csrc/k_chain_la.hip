@@ -350,6 +350,11 @@ hipError_t launch_chain_la(int storage, int loss, const ChainArgs& a, const LaPl
     if (loss == kSquared) return la_t<uint16_t, kSquared>(a, p.d, p.M, p.lds, st, tm);
     return la_t<uint16_t, kPoisson>(a, p.d, p.M, p.lds, st, tm);
   }
+  if (storage == kStoreF16) {
+    if (loss == kLogistic) return la_t<_Float16, kLogistic>(a, p.d, p.M, p.lds, st, tm);
+    if (loss == kSquared) return la_t<_Float16, kSquared>(a, p.d, p.M, p.lds, st, tm);
+    return la_t<_Float16, kPoisson>(a, p.d, p.M, p.lds, st, tm);
+  }
   if (loss == kLogistic) return la_t<float, kLogistic>(a, p.d, p.M, p.lds, st, tm);
   if (loss == kSquared) return la_t<float, kSquared>(a, p.d, p.M, p.lds, st, tm);
   return la_t<float, kPoisson>(a, p.d, p.M, p.lds, st, tm);

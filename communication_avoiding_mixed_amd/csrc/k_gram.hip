@@ -4,8 +4,9 @@
 // Linear Models on GPUs" forms the sb x sb Gram from low-precision inputs with
 // high-precision accumulation on the GPU's matrix hardware; the inner
 // recurrence only ever reads blocks G_{j,t} with t < j, so only those are
-// computed.  bf16 storage uses the MFMA tile of casgd_gram.h; float32 storage
-// runs the same tiles on the vector ALUs.
+// computed.  bf16 and fp16 rows use the MFMA tile of casgd_gram.h (bf16 or
+// fp16 MFMA); float32 rows run the same tiles on the vector ALUs.  gr rounds
+// every entry once to bf16 as it is stored (G communicated in low precision).
 #include "casgd_device.h"
 #include "casgd_gram.h"
 #include "casgd_internal.h"
@@ -17,25 +18,36 @@ using gram::kTile;
 
 // One 64 x 64 output tile per workgroup; `order` maps workgroups to tiles
 // (XCD-grouped) and holds -1 for the workgroups that pad the grid.
-template <int BK, int D>
+template <int BK, int D, bool F16>
 __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restrict__ Y,
                                                         int64_t ld, int b, int tps,
                                                         float* __restrict__ G,
-                                                        const int* __restrict__ order) {
+                                                        const int* __restrict__ order, int gr) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[gram::lds_elems<BK>()];
   const int tile = order[blockIdx.x];
   if (tile < 0) return;
-  gram::bf16_tile<BK, D>(Y, ld, b, tps, G, tile, lds);
+  gram::bf16_tile<BK, D, false, gram::SameRow, F16>(Y, ld, b, tps, G, tile, lds, gram::SameRow{}, gr != 0);
 }
 
 // float32 storage: the same tiles on the vector ALUs (casgd_gram.h).
 __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__ Y, int64_t ld,
                                                        int b, int tps, float* __restrict__ G,
-                                                       const int* __restrict__ order) {
+                                                       const int* __restrict__ order, int gr) {
   __shared__ __attribute__((aligned(16))) float lds[gram::kF32LdsElems];
   const int tile = order[blockIdx.x];
   if (tile < 0) return;
-  gram::f32_tile(Y, ld, b, tps, G, tile, lds);
+  gram::f32_tile(Y, ld, b, tps, G, tile, lds, gram::SameRow{}, gr != 0);
+}
+
+template <bool F16>
+hipError_t gram_lp(const uint16_t* Yb, int64_t ld, int b, int tps, float* G, const int* order, int gr,
+                   dim3 grid, hipStream_t st, const LaunchTimer& tm) {
+  switch (gram_variant(ld)) {
+    case 0: return launch_kernel(gram_bf16_kernel<32, 1, F16>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order, gr);
+    case 1: return launch_kernel(gram_bf16_kernel<64, 8, F16>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order, gr);
+    case 2: return launch_kernel(gram_bf16_kernel<64, 4, F16>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order, gr);
+    default: return launch_kernel(gram_bf16_kernel<64, 2, F16>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order, gr);
+  }
 }
 
 }  // namespace
@@ -78,23 +90,16 @@ std::vector<int> gram_order(int s, int b, int nx) {
   return order;
 }
 
-hipError_t launch_gram(int storage, const void* Y, int64_t ld, int s, int b, float* G,
-                       const GramPlan& plan, const int* order, hipStream_t st, const LaunchTimer& tm) {
+hipError_t launch_gram(int kind, const void* Y, int64_t ld, int s, int b, float* G,
+                       const GramPlan& plan, const int* order, int gr, hipStream_t st, const LaunchTimer& tm) {
   (void)s;
   if (plan.tiles == 0) return hipSuccess;
   const int tps = (b + kTile - 1) / kTile;
   const dim3 grid(static_cast<unsigned>(plan.slots));
-  if (storage == kStoreBF16) {
-    const uint16_t* Yb = static_cast<const uint16_t*>(Y);
-    switch (gram_variant(ld)) {
-      case 0: return launch_kernel(gram_bf16_kernel<32, 1>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
-      case 1: return launch_kernel(gram_bf16_kernel<64, 8>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
-      case 2: return launch_kernel(gram_bf16_kernel<64, 4>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
-      default: return launch_kernel(gram_bf16_kernel<64, 2>, grid, dim3(256), 0, st, tm, Yb, ld, b, tps, G, order);
-    }
-  }
+  if (kind == kStoreBF16) return gram_lp<false>(static_cast<const uint16_t*>(Y), ld, b, tps, G, order, gr, grid, st, tm);
+  if (kind == kStoreF16) return gram_lp<true>(static_cast<const uint16_t*>(Y), ld, b, tps, G, order, gr, grid, st, tm);
   return launch_kernel(gram_f32_kernel, grid, dim3(256), 0, st, tm, static_cast<const float*>(Y), ld, b,
-                       tps, G, order);
+                       tps, G, order, gr);
 }
 
 }  // namespace casgd

@@ -3,6 +3,8 @@
 // SGD for Generalized Linear Models on GPUs" compares the method with float32
 // SGD.  Margins are float32 dot products of the stored rows; loss terms and
 // all sums are float64, reduced in a fixed order (no atomics).
+#include <cmath>
+
 #include "casgd_device.h"
 #include "casgd_internal.h"
 
@@ -21,6 +23,29 @@ struct Widen<uint16_t> {
       f[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
       f[2 * e + 1] = bf16_to_f32(w[e] >> 16);
     }
+  }
+};
+template <>
+struct Widen<_Float16> {
+  static constexpr int kElems = 8;
+  __device__ static void run(const u32x4& q, float (&f)[8]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = f16_to_f32(w[e] & 0xFFFFu);
+      f[2 * e + 1] = f16_to_f32(w[e] >> 16);
+    }
+  }
+};
+// fp8 rows: the stored E4M3 values, still scaled by the matrix's 2^k (each
+// row's dot product is scaled back once, exactly)
+template <>
+struct Widen<uint8_t> {
+  static constexpr int kElems = 16;
+  __device__ static void run(const u32x4& q, float (&f)[16]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) f[e] = e4m3_to_f32((w[e / 4] >> (8 * (e % 4))) & 0xFFu);
   }
 };
 template <>
@@ -47,7 +72,7 @@ __global__ __launch_bounds__(256) void loss_kernel(const T* __restrict__ Xs,
                                                    const float* __restrict__ y, int64_t m,
                                                    int64_t n, int64_t ld,
                                                    const float* __restrict__ w,
-                                                   double* __restrict__ partial) {
+                                                   double* __restrict__ partial, float unscale) {
   constexpr int E = Widen<T>::kElems;
   constexpr int R = 2;
   __shared__ __attribute__((aligned(16))) float wl[WLDS ? kLossWlMax : 4];
@@ -96,7 +121,7 @@ __global__ __launch_bounds__(256) void loss_kernel(const T* __restrict__ Xs,
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float tot = group_sum<GS>(d[r]);
+      const float tot = group_sum<GS>(d[r]) * unscale;
       if (lane == 0 && row0 + r < m)
         acc += loss_value<LOSS>(static_cast<double>(tot), static_cast<double>(y[row0 + r]));
     }
@@ -124,7 +149,7 @@ __global__ __launch_bounds__(256) void loss_narrow_kernel(const T* __restrict__ 
                                                           const float* __restrict__ y, int64_t m,
                                                           int64_t n, int64_t ld,
                                                           const float* __restrict__ w,
-                                                          double* __restrict__ partial) {
+                                                          double* __restrict__ partial, float unscale) {
   constexpr int E = Widen<T>::kElems;
   constexpr int G = 64 / GS;
   const int lane = threadIdx.x & 63;
@@ -157,7 +182,7 @@ __global__ __launch_bounds__(256) void loss_narrow_kernel(const T* __restrict__ 
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) d = fmaf(f[e], wv[e], d);
-      const float tot = group_sum<GS>(d);
+      const float tot = group_sum<GS>(d) * unscale;
       if (c == r) mine = tot;
     }
     const int64_t myrow = base + c * G + g;
@@ -189,11 +214,11 @@ __global__ __launch_bounds__(256) void loss_finish_kernel(const double* __restri
 
 template <typename T, int LOSS, int GS>
 void loss_g(const T* X, const float* y, int64_t m, int64_t n, int64_t ld, const float* w, double* partial,
-            hipStream_t st) {
+            float unscale, hipStream_t st) {
   if (ld <= kLossWlMax)
-    loss_kernel<T, LOSS, GS, true><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+    loss_kernel<T, LOSS, GS, true><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial, unscale);
   else
-    loss_kernel<T, LOSS, GS, false><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial);
+    loss_kernel<T, LOSS, GS, false><<<kLossBlocks, 256, 0, st>>>(X, y, m, n, ld, w, partial, unscale);
 }
 
 // A narrow-kernel block takes 256 rows per pass: no more blocks than passes need.
@@ -208,44 +233,51 @@ inline int partials_for(int64_t cpr, int64_t m) { return cpr > 8 ? kLossBlocks :
 // Launches the loss kernel for this row width; returns the partial sums it writes.
 template <typename T, int LOSS>
 int loss_gs(const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld, const float* w,
-             double* partial, hipStream_t st) {
+             double* partial, float unscale, hipStream_t st) {
   const int64_t cpr = ld / Widen<T>::kElems;
   const T* X = static_cast<const T*>(Xs);
   if (cpr >= 64)
-    loss_g<T, LOSS, 64>(X, y, m, n, ld, w, partial, st);
+    loss_g<T, LOSS, 64>(X, y, m, n, ld, w, partial, unscale, st);
   else if (cpr >= 32)
-    loss_g<T, LOSS, 32>(X, y, m, n, ld, w, partial, st);
+    loss_g<T, LOSS, 32>(X, y, m, n, ld, w, partial, unscale, st);
   else if (cpr >= 16)
-    loss_g<T, LOSS, 16>(X, y, m, n, ld, w, partial, st);
+    loss_g<T, LOSS, 16>(X, y, m, n, ld, w, partial, unscale, st);
   else if (cpr > 8)
-    loss_g<T, LOSS, 8>(X, y, m, n, ld, w, partial, st);
+    loss_g<T, LOSS, 8>(X, y, m, n, ld, w, partial, unscale, st);
   else if (cpr > 4)  // the narrow kernels read chunks [0, GS) only
-    loss_narrow_kernel<T, LOSS, 8><<<narrow_blocks(m), 256, 0, st>>>(X, y, m, n, ld, w, partial);
+    loss_narrow_kernel<T, LOSS, 8><<<narrow_blocks(m), 256, 0, st>>>(X, y, m, n, ld, w, partial, unscale);
   else
-    loss_narrow_kernel<T, LOSS, 4><<<narrow_blocks(m), 256, 0, st>>>(X, y, m, n, ld, w, partial);
+    loss_narrow_kernel<T, LOSS, 4><<<narrow_blocks(m), 256, 0, st>>>(X, y, m, n, ld, w, partial, unscale);
   return partials_for(cpr, m);
 }
 
 template <typename T>
 int loss_t(int loss, const void* Xs, const float* y, int64_t m, int64_t n, int64_t ld,
-           const float* w, double* partial, hipStream_t st) {
-  if (loss == kLogistic) return loss_gs<T, kLogistic>(Xs, y, m, n, ld, w, partial, st);
-  if (loss == kSquared) return loss_gs<T, kSquared>(Xs, y, m, n, ld, w, partial, st);
-  return loss_gs<T, kPoisson>(Xs, y, m, n, ld, w, partial, st);
+           const float* w, double* partial, float unscale, hipStream_t st) {
+  if (loss == kLogistic) return loss_gs<T, kLogistic>(Xs, y, m, n, ld, w, partial, unscale, st);
+  if (loss == kSquared) return loss_gs<T, kSquared>(Xs, y, m, n, ld, w, partial, unscale, st);
+  return loss_gs<T, kPoisson>(Xs, y, m, n, ld, w, partial, unscale, st);
 }
 
 }  // namespace
 
 int loss_partials(int storage, int64_t m, int64_t ld) {
-  const int64_t cpr = storage == kStoreBF16 ? ld / Widen<uint16_t>::kElems : ld / Widen<float>::kElems;
+  const int64_t cpr = ld / (16 / elem_bytes(storage));
   return partials_for(cpr, m);
 }
 
 hipError_t launch_loss(int storage, int loss, const void* Xs, const float* y, int64_t m, int64_t n,
-                       int64_t ld, const float* w, double* partial, double* out_dev,
+                       int64_t ld, const float* w, double* partial, double* out_dev, int fp8_exp,
                        hipStream_t st) {
-  const int np = storage == kStoreBF16 ? loss_t<uint16_t>(loss, Xs, y, m, n, ld, w, partial, st)
-                                       : loss_t<float>(loss, Xs, y, m, n, ld, w, partial, st);
+  int np;
+  switch (storage) {
+    case kStoreBF16: np = loss_t<uint16_t>(loss, Xs, y, m, n, ld, w, partial, 1.f, st); break;
+    case kStoreF16: np = loss_t<_Float16>(loss, Xs, y, m, n, ld, w, partial, 1.f, st); break;
+    case kStoreF8:
+      np = loss_t<uint8_t>(loss, Xs, y, m, n, ld, w, partial, std::ldexp(1.0f, -fp8_exp), st);
+      break;
+    default: np = loss_t<float>(loss, Xs, y, m, n, ld, w, partial, 1.f, st);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   loss_finish_kernel<<<1, 256, 0, st>>>(partial, np, 1.0 / static_cast<double>(m), out_dev);

@@ -46,13 +46,14 @@ extern "C" {
 typedef struct casgd_ctx* casgd_handle;
 
 enum casgd_loss_kind { CASGD_LOGISTIC = 0, CASGD_SQUARED = 1, CASGD_POISSON = 2 };
-enum casgd_storage { CASGD_BF16 = 0, CASGD_FP32 = 1 };
+enum casgd_storage { CASGD_BF16 = 0, CASGD_FP32 = 1, CASGD_FP16 = 2, CASGD_FP8 = 3 };
 enum casgd_status { CASGD_OK = 0, CASGD_EINVAL = -1, CASGD_ENOMEM = -2, CASGD_EHIP = -3 };
 
 /* What casgd_debug_export copies out (state of the most recent outer step). */
 enum casgd_export_what {
   CASGD_EXPORT_IDX = 0, /* int32[s*b]   sampled row indices                        */
-  CASGD_EXPORT_Y = 1,   /* stored type [s*b][ld]  gathered rows (bf16 bits or f32) */
+  CASGD_EXPORT_Y = 1,   /* [s*b][ld] gathered rows: bf16 bits (bf16 and fp8
+                           storage), fp16 bits or float32                     */
   CASGD_EXPORT_YB = 2,  /* float[s*b]   gathered labels / targets                  */
   CASGD_EXPORT_G = 3,   /* float[b*b*s*(s-1)/2]  strictly-lower block triangle,     */
                         /*   block-row layout: block-row j (1 <= j < s) is a       */
@@ -83,8 +84,17 @@ enum casgd_kernel_id {
  *   m      rows, 1 <= m <= 2^31 - 1
  *   n      features, n >= 1
  *   loss   enum casgd_loss_kind
- *   storage enum casgd_storage: CASGD_BF16 rounds X to bfloat16 (round to
- *          nearest, ties to even); CASGD_FP32 keeps float32
+ *   storage enum casgd_storage, the low-precision format X is stored in (a
+ *          precision choice of the Abstract's analysis):
+ *          CASGD_BF16 bfloat16, round to nearest, ties to even;
+ *          CASGD_FP32 float32 as given;
+ *          CASGD_FP16 IEEE binary16, round to nearest even, subnormals kept,
+ *            overflow to infinity; the Gram runs on fp16 MFMA;
+ *          CASGD_FP8 OCP E4M3 of x * 2^k, round to nearest even, saturating
+ *            at 448, with one exponent k per matrix: the largest integer with
+ *            max|x| * 2^k <= 448 (casgd_fp8_exponent); the stored value
+ *            e4m3 * 2^-k is exactly a bf16 value, so the gathered rows are
+ *            bf16 and the Gram runs on bf16 MFMA.
  * The stored rows are padded with zeros to ld = n rounded up to 32 elements.
  * Synchronises the stream once so that failures surface here.
  * Returns NULL on failure (see casgd_last_error).
@@ -141,7 +151,8 @@ int casgd_outer_step_indices(casgd_handle h, int s, int b, float eta,
  *     of the second), ONE launch per step that runs the margins, recurrence
  *     and update of step k next to the Gram of step k+1 and the gather of
  *     step k+2 (timer CASGD_K_PIPE).
- * With the lookahead recurrence each step is queued as by casgd_outer_step.
+ * With the lookahead recurrence, and for fp16 and fp8 storage (whose rows
+ * go through the gather kernel), each step is queued as by casgd_outer_step.
  * The persistent launch needs every one of its workgroups resident at once
  * (one per CU); if the device cannot hold them the call fails with
  * CASGD_EHIP before anything is queued.
@@ -192,11 +203,16 @@ int casgd_export_rows(casgd_handle h, int64_t row0, int64_t nrows, void* dst_hos
 /* Padded row length (elements) of the stored data. */
 int64_t casgd_ld(casgd_handle h);
 
+/* The exponent k of fp8 storage (X stored as E4M3 of x * 2^k); 0 for the
+ * other storage types and for a NULL handle. */
+int casgd_fp8_exponent(casgd_handle h);
+
 /*
  * Bytes of the float32 Gram that the one AllReduce per outer step would carry
  * between processes (Abstract): packed != 0 gives the strictly-lower block
  * triangle (4 * b*b * s*(s-1)/2), packed == 0 the full sb x sb matrix.
  * On one process the AllReduce itself is omitted.  Returns -1 on bad input.
+ * With CASGD_OPT_GRAM_BF16 the Gram would travel as bf16: half these bytes.
  */
 int64_t casgd_gram_bytes(int s, int b, int packed);
 
@@ -246,7 +262,13 @@ enum casgd_option {
    *     workgroup's rows of G in LDS), else one launch per step;
    *   1 one launch per step.
    * Both give bit-identical results. */
-  CASGD_OPT_TRAIN_FORM = 4
+  CASGD_OPT_TRAIN_FORM = 4,
+  /* Precision in which G reaches the recurrence (a precision choice of the
+   * Abstract's analysis: the Gram communicated in low or high precision):
+   *   0 (default) float32 as accumulated (the recipe's high precision);
+   *   1 each entry rounded once to the nearest bfloat16, ties to even, as it
+   *     is stored (what a bf16 AllReduce would deliver at P = 1). */
+  CASGD_OPT_GRAM_BF16 = 5
 };
 
 /* Set an option of the handle; later outer steps use it.  EINVAL for an

@@ -431,10 +431,12 @@ def gram_choices(Y, s: int, b: int):
     """The range of admissible bf16 Gram entries when each is formed in
     float32 and rounded once: like margin_choices, a float32 dot product of
     n terms in any order is within gamma_n * sum_k |y_jk y_tk| of the exact
-    value, widened by the float32 step before the rounding.  Returns
-    (nearest, lo, hi) as dicts of blocks."""
+    value, widened by the float32 step before the rounding.  The unit
+    roundoff is taken as 2^-23, which also covers sums truncated toward zero:
+    matrix units do not specify their accumulation order or rounding.
+    Returns (nearest, lo, hi) as dicts of blocks."""
     Y = np.asarray(Y, dtype=np.float64)
-    nu = Y.shape[1] * 2.0 ** -24
+    nu = Y.shape[1] * 2.0 ** -23
     G = gram_blocks(Y, s, b)
     A = np.abs(Y)
     near, lo, hi = {}, {}, {}

@@ -5,6 +5,7 @@ placed in memory turn each access into a round trip to HBM), and kernels that
 are not written to use LDS must not get LDS from the compiler promoting local
 arrays there."""
 
+import concurrent.futures
 import os
 import re
 import shutil
@@ -22,8 +23,6 @@ HOST_ONLY = ("casgd_api.hip", "k_step.hip")
 
 def _kernels(src):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    if not os.path.exists(hipcc):
-        pytest.skip("hipcc not available")
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
         flags = [f for f in B.FLAGS if f not in ("-fPIC",)]
@@ -40,9 +39,19 @@ def _kernels(src):
     return meta
 
 
+@pytest.fixture(scope="module")
+def compiled():
+    """Device assembly metadata of every source, compiled in parallel."""
+    if not os.path.exists(shutil.which("hipcc") or "/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    workers = max(1, min(len(B.SOURCES), os.cpu_count() or 4, 8))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        return dict(zip(B.SOURCES, ex.map(_kernels, B.SOURCES)))
+
+
 @pytest.mark.parametrize("src", B.SOURCES)
-def test_no_scratch_and_no_stray_lds(src):
-    meta = _kernels(src)
+def test_no_scratch_and_no_stray_lds(src, compiled):
+    meta = compiled[src]
     if src in HOST_ONLY:
         return
     assert meta, f"no kernels found in {src}"

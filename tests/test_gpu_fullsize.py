@@ -143,3 +143,59 @@ def test_fp32_sgd_baseline_at_epsilon_shape():
     assert f_gpu < math.log(2.0)
     assert gap <= LOSS_GAP
     h.close()
+
+
+VARIANTS = {"fp16": ("fp16", 0), "fp8": ("fp8", 0), "gram-bf16": (None, 1)}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_full_size_precision_variant(name, variant):
+    """fp16 storage, fp8 storage and the bf16-communicated Gram at full size:
+    one outer step from seeded weights against the oracle (G, v, z, r, w
+    within 1e-4; for the bf16 Gram, z, r and w on the GPU's own admissible
+    G), then the whole run from w = 0 against float64 SGD on the float32
+    data over the same minibatches (final loss within 0.5%)."""
+    import torch
+    wl = synth.WORKLOADS[name]
+    storage, gbf16 = VARIANTS[variant]
+    storage = storage or wl.storage
+    X, y = synth.make_data(name)
+    h = B.CASGD(torch_dev(X), torch_dev(y), wl.loss, storage)
+    h.set_option(B.OPT_GRAM_BF16, gbf16)
+    k = O.fp8_exponent_of(X) if storage == "fp8" else None
+    if k is not None:
+        assert h.fp8_exponent == k
+    w0 = synth.make_w0(name, 3)
+    w = torch_dev(w0)
+    seed = O.step_seed(0, 11)
+    h.outer_step(wl.s, wl.b, wl.eta, seed, w)
+    gram = "bf16" if gbf16 else "fp32"
+    ref = O.outer_step(X, y, w0.astype(np.float64), wl.s, wl.b, wl.eta, seed, wl.loss, storage=storage,
+                       gram=gram, fp8_exp=k)
+    if gbf16:
+        G = {key: g.astype(np.float64) for key, g in B.unpack_gram(h.export(B.EXPORT_G), wl.s, wl.b).items()}
+        near, lo, hi = O.gram_choices(ref["Y"], wl.s, wl.b)
+        for key, g in G.items():
+            assert np.all((lo[key] <= g) & (g <= hi[key])), key
+        ref = O.outer_step_rows(ref["Y"], ref["yB"], w0.astype(np.float64), wl.s, wl.b, wl.eta, wl.loss, G=G)
+        errs = {}
+    else:
+        errs = {"G": check_gram(h.export(B.EXPORT_G), ref["Y"], wl.s, wl.b, wl.n),
+                "v": rel_l2(h.export(B.EXPORT_V), ref["v"])}
+    errs.update({"z": rel_l2(h.export(B.EXPORT_Z), ref["z"]), "r": rel_l2(h.export(B.EXPORT_R), ref["r"]),
+                 "w": rel_l2(w.cpu().numpy(), ref["w"])})
+    for key, e in errs.items():
+        assert e <= REL_TOL, (key, e)
+
+    wt = torch.zeros(wl.n, device="cuda")
+    h.train(wl.s, wl.b, wl.eta, 0, 0, wl.outer, wt)
+    f_gpu = h.loss_value(wt)
+    w_sgd = O.train(X, y, np.zeros(wl.n), wl.s, wl.b, wl.eta, wl.loss, base_seed=0,
+                    n_outer=wl.outer, storage="fp32", method="sgd")
+    f_ref = O.full_loss(X, y, w_sgd, wl.loss, storage="fp32")
+    gap = abs(f_gpu - f_ref) / abs(f_ref)
+    print(f"{name} {variant}: step errs {({key: f'{v:.1e}' for key, v in errs.items()})} "
+          f"final loss {f_gpu:.6f} vs float64 SGD {f_ref:.6f}, gap {gap:.2e}", flush=True)
+    assert gap <= LOSS_GAP
+    h.close()
