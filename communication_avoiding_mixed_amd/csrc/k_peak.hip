@@ -14,17 +14,24 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kChains = 4;  // independent accumulators per wave
 
-// 16-byte words, grid-stride, four loads in flight per thread before the stores
+// 16-byte words, grid-stride, four loads in flight per thread before the
+// stores, all marked nontemporal (streamed data: no reuse to cache).  On
+// MI355X this form on 64 workgroups per CU measured fastest among grid sizes
+// of 8 to 64 per CU, 2 to 8 loads in flight and contiguous per-workgroup
+// spans, and above hipMemcpy's device-to-device copy.
 __global__ __launch_bounds__(kThreads) void peak_copy_kernel(const u32x4_t* __restrict__ src,
                                                              u32x4_t* __restrict__ dst, int64_t n16) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4_t a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    dst[i] = a;
-    dst[i + stride] = b;
-    dst[i + 2 * stride] = c;
-    dst[i + 3 * stride] = d;
+    const u32x4_t a = __builtin_nontemporal_load(&src[i]);
+    const u32x4_t b = __builtin_nontemporal_load(&src[i + stride]);
+    const u32x4_t c = __builtin_nontemporal_load(&src[i + 2 * stride]);
+    const u32x4_t d = __builtin_nontemporal_load(&src[i + 3 * stride]);
+    __builtin_nontemporal_store(a, &dst[i]);
+    __builtin_nontemporal_store(b, &dst[i + stride]);
+    __builtin_nontemporal_store(c, &dst[i + 2 * stride]);
+    __builtin_nontemporal_store(d, &dst[i + 3 * stride]);
   }
   for (; i < n16; i += stride) dst[i] = src[i];
 }
@@ -58,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void peak_mfma_kernel(int iters, float* _
 hipError_t launch_peak_copy(const void* src, void* dst, int64_t bytes, int cus, hipStream_t stream) {
   const int64_t n16 = bytes / 16;
   if (n16 <= 0) return hipSuccess;
-  int64_t grid = static_cast<int64_t>(cus) * 8;
+  int64_t grid = static_cast<int64_t>(cus) * 64;
   const int64_t need = (n16 + kThreads - 1) / kThreads;
   if (grid > need) grid = need;
   hipLaunchKernelGGL(peak_copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
