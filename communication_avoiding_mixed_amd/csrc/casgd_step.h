@@ -28,9 +28,9 @@
 // the polls.  Waves 1..3 fold each block t of r into the per-lane partial
 // sums acc_k of blocks k >= t+2 (block k to wave 1 + k mod 3); wave 3 also
 // accumulates the update of the workgroup's column slice as r arrives.
-// r travels as 64-bit words tagged with the launch epoch, one copy per
-// reading workgroup; with every chain workgroup on one XCD (ChainArgs::place)
-// through that XCD's L2.  Every wait is bounded.  All sums run in fixed
+// r travels as 64-bit words tagged with the launch epoch, written once into
+// one array that every chain workgroup polls; with every chain workgroup on
+// one XCD (ChainArgs::place) through that XCD's L2.  Every wait is bounded.  All sums run in fixed
 // orders, so results are bit-reproducible.
 #pragma once
 
@@ -125,7 +125,7 @@ struct Rec {
   float c;
   uint32_t tag;                        // tag of this step's exchanged words
   const unsigned long long* vbox;      // margins of the step, tagged, by row
-  unsigned long long* xbuf;            // mailboxes of r: Q x s*b words
+  unsigned long long* xbuf;            // r of every row, s*b tagged words (one array for all readers)
   bool xl;                             // r goes out with plain stores (one XCD)
   float *z, *r, *w;                    // exported z, r; weights (in place)
   unsigned long long* wbox;            // tagged copy of the new weights, or nullptr
@@ -242,7 +242,9 @@ __device__ __forceinline__ void recurrence(const Rec& R, const RecLds& S, RowPtr
   int& abort_flag = *S.abort_flag;
   int& r_ready = *S.r_ready;
   int* acc_ready = S.acc_ready;
-  const unsigned long long* mbox = R.xbuf + static_cast<int64_t>(q) * sb;
+  // every workgroup publishes each of its own rows' r once; every reader
+  // polls the same words (one mailbox for the whole launch)
+  const unsigned long long* mbox = R.xbuf;
   // update plan (the same in every wave): chunks [ch0, ch1) of w
   constexpr int E = Elems<T>::E;
   const int cpr = static_cast<int>(R.ld / E);
@@ -266,15 +268,6 @@ __device__ __forceinline__ void recurrence(const Rec& R, const RecLds& S, RowPtr
       float v = 0.f;
       if (t < nown) v = chain::take(&R.vbox[j * b + q + Q * t], R.tag, R.status, &abort_flag, 0, R.spin);
       vown[p] = v;
-    }
-    // where lane l publishes: entries e = l, l + 64, ... < NO Q are (row t =
-    // e / Q, reader e % Q)
-    int et[NO], ed[NO];
-#pragma unroll
-    for (int k = 0; k < NO; ++k) {
-      const int e = lane + 64 * k;
-      et[k] = e / Q;
-      ed[k] = e - et[k] * Q;
     }
     float rp[CP];
 #pragma unroll
@@ -333,15 +326,13 @@ __device__ __forceinline__ void recurrence(const Rec& R, const RecLds& S, RowPtr
         zz[t] = vj[t] - R.c * part[t];
         rv[t] = dloss(R.loss, zz[t], yj[t]);
       }
-      // one copy of each own row's r per reader
-#pragma unroll
-      for (int k = 0; k < NO; ++k) {
-        if (64 * k >= NO * Q) break;
+      // each own row's r once, lane t for own row t: NO stores per workgroup
+      // (a copy per reader, NO * Q stores, measured 2-7% slower)
+      {
         float x = rv[0];
 #pragma unroll
-        for (int t = 1; t < NO; ++t) x = et[k] == t ? rv[t] : x;
-        if (et[k] < nown && lane + 64 * k < NO * Q)
-          chain::put_x(&R.xbuf[static_cast<int64_t>(ed[k]) * sb + jb + q + Q * et[k]], tagged(R.tag, x), R.xl);
+        for (int t = 1; t < NO; ++t) x = lane == t ? rv[t] : x;
+        if (lane < nown) chain::put_x(&R.xbuf[jb + q + Q * lane], tagged(R.tag, x), R.xl);
       }
       // the exported z and r
       if (lane == 0) {

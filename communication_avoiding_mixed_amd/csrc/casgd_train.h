@@ -54,7 +54,7 @@ struct TrainArgs {
   float* w;              // weights, in place
   float *v, *z, *r;      // exported margins, z and r of the latest step
   float* G[kRing];       // ring of G buffers (block-row layout)
-  unsigned long long* xbuf;   // r mailboxes, Q x s*b words
+  unsigned long long* xbuf;   // r of every row, s*b tagged words
   unsigned long long* vbox;   // margins, s*b words
   unsigned long long* wbox;   // new weights, n words
   unsigned long long* place;  // XCD of each chain workgroup
