@@ -555,7 +555,7 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
 
   const int Q = cp.Q;
   const bool fast = casgd::chain_fast(s, b, Q, h->ld);
-  const int64_t cpr = h->ld / (h->storage == CASGD_BF16 ? 8 : 4);  // 16-byte chunks per row
+  const int64_t cpr = h->ld / (16 / static_cast<int64_t>(h->esize));  // 16-byte chunks of a stored row
   const int gs = casgd::gather::group_size(cpr);
   const int rows_per_wg = 256 / gs;
   const int gather_wgs_all = (sb + rows_per_wg - 1) / rows_per_wg;
@@ -624,9 +624,12 @@ int run_train_pipe(casgd_ctx* h, int s, int b, float eta, uint64_t base_seed, ui
       p.idx_out = A.idx;
       p.Yo = A.Y;
       p.yBo = A.yB;
+      p.gf8 = h->storage == CASGD_FP8 ? 1 : 0;
+      p.unscale = std::ldexp(1.0f, -h->fp8_exp);
     }
+    p.gbf16 = h->gram_bf16;
     e = timed(h, CASGD_K_PIPE, [&](const casgd::LaunchTimer& tm) {
-      return cp.lean ? casgd::launch_step(h->storage, h->loss, p, h->stream, tm)
+      return cp.lean ? casgd::launch_step(casgd::row_kind(h->storage), h->loss, p, h->stream, tm)
                      : casgd::launch_pipe(h->storage, h->loss, p, h->stream, tm);
     });
     if (e != hipSuccess) return launch_fail(e, "pipelined step launch");
@@ -881,14 +884,16 @@ int casgd_train(casgd_handle h, int s, int b, float eta, uint64_t base_seed, uin
   int rc = check_step_args(h, s, b, w);
   if (rc != CASGD_OK) return rc;
   if (n_outer < 0) return fail(CASGD_EINVAL, "n_outer must be >= 0");
-  // the pipelined and persistent launches read stored rows themselves: bf16
-  // and float32 storage; fp16 and fp8 rows go through the gather each step
+  // The persistent launch and the general pipelined kernel read bf16 or
+  // float32 stored rows themselves; the pipelined launch of the lean
+  // recurrence also gathers fp16 rows and widens fp8 rows.  Other cases run
+  // step by step.
   const bool fused = h->storage == CASGD_BF16 || h->storage == CASGD_FP32;
-  if (n_outer > 0 && h->recurrence != 2 && fused) {
+  if (n_outer > 0 && h->recurrence != 2) {
     const casgd::ChainPlan cp = plan_chain(h, s, b);
-    if (cp.lean && h->train_form == 0 && persist_margin_rows(h, cp, s, b) > 0)
+    if (fused && cp.lean && h->train_form == 0 && persist_margin_rows(h, cp, s, b) > 0)
       return run_train_persist(h, cp, s, b, eta, base_seed, first_step, n_outer, w);
-    return run_train_pipe(h, s, b, eta, base_seed, first_step, n_outer, w);
+    if (fused || cp.lean) return run_train_pipe(h, s, b, eta, base_seed, first_step, n_outer, w);
   }
   for (int k = 0; k < n_outer; ++k) {
     rc = run_outer(h, s, b, eta, casgd::splitmix64(base_seed, first_step + k), nullptr, w);

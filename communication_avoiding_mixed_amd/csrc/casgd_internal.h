@@ -161,9 +161,11 @@ struct PipeArgs {
   const int* order = nullptr;
   int gbf16 = 0;  // the Gram role rounds each entry of G once to bf16
   int gath0 = 0, gath_wgs = 0, gs = 0;  // gs: lanes per row (gather::group_size)
+  int gf8 = 0;          // stored rows are fp8: widened to bf16 (times unscale) as they are gathered
+  float unscale = 1.f;  // 2^-k of fp8 storage
   const void* Xs = nullptr;
   const float* y = nullptr;
-  int64_t m = 0, cpr = 0;
+  int64_t m = 0, cpr = 0;  // cpr: 16-byte chunks of a stored row
   int sb = 0;
   uint64_t seed = 0;  // seed of step k+2
   int32_t* idx_out = nullptr;

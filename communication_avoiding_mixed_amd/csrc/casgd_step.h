@@ -609,15 +609,20 @@ __device__ __forceinline__ void margins(const PipeArgs& p, int m) {
 template <int GS>
 __device__ __forceinline__ void gather_rows(const PipeArgs& p, int g) {
   constexpr int RPW = kThreads / GS;  // rows per workgroup pass
-  for (int row0 = g * RPW; row0 < p.sb; row0 += p.gath_wgs * RPW)
-    gather::copy_row<GS>(static_cast<const u32x4*>(p.Xs), p.y, p.m, p.cpr, p.sb, p.seed, nullptr,
-                         p.idx_out, static_cast<u32x4*>(p.Yo), p.yBo,
-                         row0 + static_cast<int>(threadIdx.x) / GS, threadIdx.x % GS);
+  for (int row0 = g * RPW; row0 < p.sb; row0 += p.gath_wgs * RPW) {
+    const int row = row0 + static_cast<int>(threadIdx.x) / GS;
+    if (p.gf8)
+      gather::copy_row_f8<GS>(static_cast<const u32x4*>(p.Xs), p.y, p.m, p.cpr, p.sb, p.seed, nullptr, p.idx_out,
+                              static_cast<u32x4*>(p.Yo), p.yBo, p.unscale, row, threadIdx.x % GS);
+    else
+      gather::copy_row<GS>(static_cast<const u32x4*>(p.Xs), p.y, p.m, p.cpr, p.sb, p.seed, nullptr, p.idx_out,
+                           static_cast<u32x4*>(p.Yo), p.yBo, row, threadIdx.x % GS);
+  }
 }
 
-// T = uint16_t: bf16 rows, Gram on MFMA with (BK, D) stages; T = _Float16:
-// fp16 rows (margins and recurrence only: no Gram role); T = float: float32
-// rows, Gram on the vector ALUs (BK, D unused).
+// T = uint16_t: bf16 rows, Gram on bf16 MFMA with (BK, D) stages; T =
+// _Float16: fp16 rows, Gram on fp16 MFMA; T = float: float32 rows, Gram on
+// the vector ALUs (BK, D unused).
 template <typename T, int NO, int CP, int BK, int D>
 __global__ __launch_bounds__(kThreads) void step_kernel(PipeArgs p, int loss) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
@@ -648,9 +653,10 @@ __global__ __launch_bounds__(kThreads) void step_kernel(PipeArgs p, int loss) {
       if constexpr (std::is_same<T, float>::value)
         gram::f32_tile(static_cast<const float*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile, sm, gram::SameRow{},
                        p.gbf16 != 0);
-      else if constexpr (std::is_same<T, uint16_t>::value)
-        gram::bf16_tile<BK, D>(static_cast<const uint16_t*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile,
-                               reinterpret_cast<uint16_t*>(sm), gram::SameRow{}, p.gbf16 != 0);
+      else
+        gram::bf16_tile<BK, D, false, gram::SameRow, std::is_same<T, _Float16>::value>(
+            static_cast<const uint16_t*>(p.gY), p.a.ld, p.a.b, p.tps, p.gG, tile, reinterpret_cast<uint16_t*>(sm),
+            gram::SameRow{}, p.gbf16 != 0);
     }
     return;
   }
@@ -699,8 +705,12 @@ hipError_t launch_variant(int storage, int loss, const PipeArgs& p, int grid, si
                           const LaunchTimer& tm) {
   if (storage == kStoreF32) return launch_t<float, NO, CP, 0, 0>(p, loss, grid, lds, st, tm);
   if (storage == kStoreF16) {
-    if (p.gram_slots > 0) return hipErrorInvalidValue;  // fp16 rows: no Gram role here
-    return launch_t<_Float16, NO, CP, 0, 0>(p, loss, grid, lds, st, tm);
+    switch (gram_variant(p.a.ld)) {
+      case 0: return launch_t<_Float16, NO, CP, 32, 1>(p, loss, grid, lds, st, tm);
+      case 1: return launch_t<_Float16, NO, CP, 64, 8>(p, loss, grid, lds, st, tm);
+      case 2: return launch_t<_Float16, NO, CP, 64, 4>(p, loss, grid, lds, st, tm);
+      default: return launch_t<_Float16, NO, CP, 64, 2>(p, loss, grid, lds, st, tm);
+    }
   }
   switch (gram_variant(p.a.ld)) {
     case 0: return launch_t<uint16_t, NO, CP, 32, 1>(p, loss, grid, lds, st, tm);

@@ -156,55 +156,14 @@ __global__ __launch_bounds__(256) void gather_kernel(
   gather::copy_row<GS>(Xs, y, m, cpr, sb, seed, idx_in, idx_out, Y, yB, row, threadIdx.x % GS);
 }
 
-// Sample + gather of fp8 rows, widened to bf16: the stored value e4m3 * 2^-k
-// has at most four significant bits and stays in bf16's range, so the bf16
-// row holds exactly the stored values and every later kernel runs the bf16
-// path on them.  A group of GS lanes reads 16-byte chunks of 16 fp8 values
-// and writes two 16-byte chunks of 8 bf16 each.
+// Sample + gather of fp8 rows, widened to bf16 (gather::copy_row_f8).
 template <int GS>
 __global__ __launch_bounds__(256) void gather_f8_kernel(
     const u32x4* __restrict__ Xs, const float* __restrict__ y, int64_t m, int64_t cpr8, int sb,
     uint64_t seed, const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx_out,
     u32x4* __restrict__ Y, float* __restrict__ yB, float unscale) {
-  constexpr int U = 4;
   const int row = blockIdx.x * (256 / GS) + threadIdx.x / GS;
-  const int lane = threadIdx.x % GS;
-  if (row >= sb) return;
-  int64_t src = idx_in ? static_cast<int64_t>(idx_in[row])
-                       : static_cast<int64_t>(sample_row(seed, static_cast<uint64_t>(row),
-                                                         static_cast<uint64_t>(m)));
-  src = src < 0 ? 0 : (src >= m ? m - 1 : src);
-  if (lane == 0) {
-    idx_out[row] = static_cast<int32_t>(src);
-    yB[row] = y[src];
-  }
-  const u32x4* xr = Xs + src * cpr8;
-  u32x4* yr = Y + static_cast<int64_t>(row) * cpr8 * 2;
-  for (int64_t c0 = lane; c0 < cpr8; c0 += GS * U) {
-    u32x4 q[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + GS * u;
-      q[u] = c < cpr8 ? xr[c] : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + GS * u;
-      if (c >= cpr8) break;
-      const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-      uint32_t o[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t lo = f32_to_bf16(e4m3_to_f32((w[i] >> (16 * h)) & 0xFFu) * unscale);
-          const uint32_t hi = f32_to_bf16(e4m3_to_f32((w[i] >> (16 * h + 8)) & 0xFFu) * unscale);
-          o[2 * i + h] = lo | (hi << 16);
-        }
-      yr[2 * c] = u32x4{o[0], o[1], o[2], o[3]};
-      yr[2 * c + 1] = u32x4{o[4], o[5], o[6], o[7]};
-    }
-  }
+  gather::copy_row_f8<GS>(Xs, y, m, cpr8, sb, seed, idx_in, idx_out, Y, yB, unscale, row, threadIdx.x % GS);
 }
 
 template <int GS>

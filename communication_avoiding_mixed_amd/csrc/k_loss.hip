@@ -32,8 +32,8 @@ struct Widen<_Float16> {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      f[2 * e] = f16_to_f32(w[e] & 0xFFFFu);
-      f[2 * e + 1] = f16_to_f32(w[e] >> 16);
+      f[2 * e] = f16_to_f32_hw(w[e] & 0xFFFFu);
+      f[2 * e + 1] = f16_to_f32_hw(w[e] >> 16);
     }
   }
 };

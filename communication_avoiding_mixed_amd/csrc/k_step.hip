@@ -59,7 +59,7 @@ hipError_t launch_step(int storage, int loss, const PipeArgs& p, hipStream_t st,
   size_t lds = static_cast<size_t>(step::layout(p.a.s, p.a.b, NO, CP).total) * sizeof(float);
   // the margin workgroups stage w in LDS, the Gram's tiles their stages
   const size_t wl = p.a.ld <= chain::kWlMax ? sizeof(float) * p.a.ld : 0;
-  const size_t glds = storage != kStoreBF16 ? sizeof(float) * gram::kF32LdsElems
+  const size_t glds = storage == kStoreF32 ? sizeof(float) * gram::kF32LdsElems
                       : sizeof(uint16_t) * (gram_variant(p.a.ld) == 0 ? gram::lds_elems<32>() : gram::lds_elems<64>());
   if (wl > lds) lds = wl;
   if (p.gram_slots > 0 && glds > lds) lds = glds;

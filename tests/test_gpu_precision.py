@@ -137,3 +137,45 @@ def test_bf16_gram_step(storage, loss, m, n, s, b):
         for key, got in (("z", h.export(B.EXPORT_Z)), ("r", h.export(B.EXPORT_R)), ("w", w.cpu().numpy())):
             assert rel_l2(got, want[key]) <= REL_TOL, key
     h.close()
+
+
+@pytest.mark.parametrize("form", [B.TRAIN_PERSISTENT, B.TRAIN_PER_STEP])
+@pytest.mark.parametrize("storage", ["bf16", "fp16", "fp8", "fp32"])
+@pytest.mark.parametrize("m,n,s,b", [(2000, 300, 4, 64), (3000, 45, 6, 20)])
+def test_bf16_gram_train_equals_its_outer_steps(storage, form, m, n, s, b):
+    # every launch form of casgd_train rounds G like the single outer step
+    # (the pipelined launch's Gram role included)
+    X, y, w0 = data(m, n, "logistic", 5)
+    h = B.CASGD(torch_dev(X), torch_dev(y), "logistic", storage)
+    h.set_option(B.OPT_GRAM_BF16, 1)
+    h.set_option(B.OPT_TRAIN_FORM, form)
+    w1, w2 = torch_dev(w0), torch_dev(w0)
+    h.train(s, b, 0.5, 9, 2, 5, w1)
+    for k in range(2, 7):
+        h.outer_step(s, b, 0.5, B.step_seed(9, k), w2)
+    torch.cuda.synchronize()
+    assert torch.equal(w1, w2)
+    h.close()
+
+
+def test_fp16_rows_decode_exactly_subnormals_included():
+    # column 3 holds binary16 subnormals k * 2^-24 (and -k * 2^-24); with w
+    # the unit vector of that column every margin is one decoded value
+    # (the other products are exact zeros), so it must equal the oracle's
+    # stored value bit for bit
+    rng = np.random.default_rng(10)
+    m, n, s, b = 900, 40, 3, 64
+    X = (rng.standard_normal((m, n)) / np.sqrt(n)).astype(np.float32)
+    X[:, 3] = (rng.integers(1, 1024, m) * 2.0 ** -24 * rng.choice([-1.0, 1.0], m)).astype(np.float32)
+    X[::7, 3] = np.float32(2.0 ** -14 * 1.5)  # and a few normals
+    y = rng.choice([-1.0, 1.0], m).astype(np.float32)
+    h = B.CASGD(torch_dev(X), torch_dev(y), "logistic", "fp16")
+    w0 = np.zeros(n, np.float32)
+    w0[3] = 1.0
+    w = torch_dev(w0)
+    h.outer_step(s, b, 0.5, O.step_seed(3, 0), w)
+    idx = h.export(B.EXPORT_IDX).astype(np.int64)
+    v = h.export(B.EXPORT_V).astype(np.float64)
+    assert np.array_equal(v, O.f16_round(X[idx, 3]))
+    assert np.any(np.abs(v) < 2.0 ** -14)  # subnormals were among the sampled rows
+    h.close()
