@@ -218,7 +218,12 @@ def measure_peaks():
     dst = torch.empty_like(src)
     t_copy = best(lambda: B.peak_copy(src, dst), 10)
     ok = bool(torch.equal(src, dst))
-    del src, dst
+    del dst
+    rwgs = torch.cuda.get_device_properties(0).multi_processor_count * 4
+    rout = torch.zeros(rwgs * 8, device="cuda:0")
+    t_read = best(lambda: B.peak_read(src, rout, rwgs), 10)
+    ok_read = bool(torch.all(rout == 1.0))
+    del src, rout
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     wgs, iters = 2 * cus, 20000
     out = torch.empty(wgs * 256, device="cuda:0")
@@ -230,6 +235,10 @@ def measure_peaks():
         "hbm_copy_GB/s": 2 * nbytes / t_copy / 1e9,
         "hbm_copy_frac_of_datasheet": 2 * nbytes / t_copy / 1e9 / PEAK_HBM_GBS,
         "copy": f"calibration copy kernel, 1 GiB read + 1 GiB written, best of 10, result checked: {ok}",
+        "hbm_read_GB/s": nbytes / t_read / 1e9,
+        "hbm_read_frac_of_datasheet": nbytes / t_read / 1e9 / PEAK_HBM_GBS,
+        "read": f"read calibration kernel (direct-to-LDS, {rwgs} workgroups), 1 GiB, best of 10, "
+                f"data checked: {ok_read}",
         "mfma_bf16_TFLOP/s": flops / t_mfma / 1e12,
         "mfma_bf16_frac_of_datasheet": flops / t_mfma / 1e12 / PEAK_BF16_TFLOPS,
         "mfma": f"{wgs} workgroups x 4 waves x 4 independent chains x {iters} "

@@ -54,6 +54,7 @@ SIGNATURES = {
     "casgd_loss_noalloc": (_I, [_VP, _VP, _VP]),
     "casgd_peak_copy": (_I, [_VP, _VP, _I64, _VP]),
     "casgd_peak_mfma": (_I, [_VP, _I, _I, _VP]),
+    "casgd_peak_read": (_I, [_VP, _I64, _VP, _I, _VP]),
 }
 
 _lib = None
@@ -121,6 +122,20 @@ def peak_copy(src, dst):
         raise ValueError("src and dst must have the same byte size")
     _check(load().casgd_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
                                   nbytes, _stream_ptr()), "casgd_peak_copy")
+    return nbytes
+
+
+def peak_read(src, out, workgroups: int):
+    """Stream src (a contiguous GPU tensor) with the read calibration kernel
+    on torch's current stream; out: float32 GPU tensor of workgroups * 8.
+    Returns the bytes read."""
+    import torch
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    _dev_f32(out, (workgroups * 8,), "out")
+    nbytes = src.numel() * src.element_size()
+    _check(load().casgd_peak_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                                  workgroups, _stream_ptr()), "casgd_peak_read")
     return nbytes
 
 

@@ -666,6 +666,15 @@ int casgd_peak_copy(const void* src, void* dst, int64_t bytes, void* hip_stream)
   return e == hipSuccess ? CASGD_OK : hip_fail(e, "copy calibration launch");
 }
 
+int casgd_peak_read(const void* src, int64_t bytes, float* out, int workgroups, void* hip_stream) {
+  if (!src || !out) return fail(CASGD_EINVAL, "NULL pointer");
+  if (bytes < 16 || bytes % 16 != 0) return fail(CASGD_EINVAL, "bytes must be a positive multiple of 16");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return fail(CASGD_EINVAL, "src must be 16-byte aligned");
+  if (workgroups < 1 || workgroups > (1 << 20)) return fail(CASGD_EINVAL, "workgroups must be in [1, 2^20]");
+  hipError_t e = casgd::launch_peak_read(src, bytes, out, workgroups, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? CASGD_OK : hip_fail(e, "read calibration launch");
+}
+
 int casgd_peak_mfma(float* out, int workgroups, int iters, void* hip_stream) {
   if (!out) return fail(CASGD_EINVAL, "NULL pointer");
   if (workgroups < 1 || workgroups > (1 << 20) || iters < 1)

@@ -220,5 +220,8 @@ int loss_partials(int storage, int64_t m, int64_t ld);
 // (32x32x16) per wave, each lane's accumulator sum written to out.
 hipError_t launch_peak_copy(const void* src, void* dst, int64_t bytes, int cus, hipStream_t stream);
 hipError_t launch_peak_mfma(float* out, int workgroups, int iters, hipStream_t stream);
+// workgroups read bytes (a multiple of 16) of src, each a contiguous slice,
+// with direct-to-LDS loads; out[workgroups * 8] receives ring words.
+hipError_t launch_peak_read(const void* src, int64_t bytes, float* out, int workgroups, hipStream_t stream);
 
 }  // namespace casgd

@@ -36,6 +36,28 @@ __global__ __launch_bounds__(kThreads) void peak_copy_kernel(const u32x4_t* __re
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Read-only streaming: workgroup w reads its slice of src with direct-to-LDS
+// loads (no register results, so every wave keeps its loads in flight) into
+// an 8 KB ring, then writes the first word of each ring slot it holds, so
+// the data is checked and nothing is optimised away.
+__global__ __launch_bounds__(kThreads) void peak_read_kernel(const u32x4_t* __restrict__ src, int64_t n16,
+                                                             float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) u32x4_t ring[8][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
+  int k = 0;
+  for (int64_t c0 = b0 + static_cast<int64_t>(wave) * 64; c0 < b1; c0 += 64 * (kThreads / 64), ++k)
+    if (c0 + lane < b1)
+      __builtin_amdgcn_global_load_lds(src + c0 + lane, (lds_void*)(&ring[(2 * wave + (k & 1)) & 7][0]), 16, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x < 8) out[static_cast<int64_t>(blockIdx.x) * 8 + threadIdx.x] = __uint_as_float(ring[threadIdx.x][0].x);
+}
+
 // iters x kChains dependent v_mfma_f32_32x32x16_bf16 per wave; each lane
 // writes the sum of its accumulators so that nothing is optimised away
 __global__ __launch_bounds__(kThreads) void peak_mfma_kernel(int iters, float* __restrict__ out) {
@@ -70,6 +92,12 @@ hipError_t launch_peak_copy(const void* src, void* dst, int64_t bytes, int cus, 
   if (grid > need) grid = need;
   hipLaunchKernelGGL(peak_copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
                      static_cast<const u32x4_t*>(src), static_cast<u32x4_t*>(dst), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_peak_read(const void* src, int64_t bytes, float* out, int workgroups, hipStream_t stream) {
+  hipLaunchKernelGGL(peak_read_kernel, dim3(workgroups), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4_t*>(src), bytes / 16, out);
   return hipGetLastError();
 }
 

@@ -302,6 +302,13 @@ int casgd_get_timing(casgd_handle h, int kernel, double* total_ms, int64_t* laun
  * iters * 32768 flops: the achievable dense bf16 matrix-core rate under
  * sustained load.  EINVAL for workgroups outside [1, 2^20] or iters < 1. */
 int casgd_peak_copy(const void* src, void* dst, int64_t bytes, void* hip_stream);
+/* casgd_peak_read: `workgroups` workgroups of 256 lanes read `bytes` (a
+ * positive multiple of 16) of device src, 16-byte aligned, each a contiguous
+ * slice, with direct-to-LDS loads (the achievable HBM read rate); workgroup
+ * w writes 8 words of its LDS ring to device out[8 w .. 8 w + 7] (all of
+ * them read from src when each slice spans at least 8 x 64 x 16 bytes).
+ * EINVAL for bad sizes, alignment or workgroup count. */
+int casgd_peak_read(const void* src, int64_t bytes, float* out, int workgroups, void* hip_stream);
 int casgd_peak_mfma(float* out, int workgroups, int iters, void* hip_stream);
 
 /* Text of the last error on the calling thread ("" if none). */

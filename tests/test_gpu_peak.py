@@ -44,3 +44,16 @@ def test_calibration_mfma_sum_has_its_closed_form():
     ptr = ctypes.c_void_p(out.data_ptr())
     assert lib.casgd_peak_mfma(ptr, 0, iters, None) == B.EINVAL
     assert lib.casgd_peak_mfma(ptr, wgs, 0, None) == B.EINVAL
+
+
+def test_calibration_read_lands_the_data():
+    # 1 MiB of 1.0 over 16 workgroups: every slice spans 4096 chunks, so all
+    # 8 ring slots a workgroup reports were filled from src
+    src = torch.ones(1 << 18, device="cuda:0")
+    out = torch.zeros(16 * 8, device="cuda:0")
+    assert B.peak_read(src, out, 16) == src.numel() * 4
+    torch.cuda.synchronize()
+    assert torch.all(out == 1.0)
+    lib = B.load()
+    assert lib.casgd_peak_read(ctypes.c_void_p(src.data_ptr()), 12, ctypes.c_void_p(out.data_ptr()), 16,
+                               None) == B.EINVAL
