@@ -134,6 +134,19 @@ struct Rec {
   long spin;
 };
 
+// Whether the update runs overlapped with the recurrence, on the last wave
+// (at most 64 chunks of w per workgroup and kUR rows per lane per block);
+// otherwise the whole workgroup runs it afterwards.  E: elements per chunk.
+__host__ __device__ inline bool update_overlapped(int b, int Q, int64_t ld, int E) {
+  const int64_t cpr = ld / E;
+  const int64_t per = (cpr + Q - 1) / Q;
+  int cw = 1;
+  while (cw < per && cw < 64) cw <<= 1;
+  const int rgw = 64 / cw;
+  const int rpl = (b + rgw - 1) / rgw;
+  return per <= 64 && rpl <= kUR;
+}
+
 struct RecLds {
   float *rs, *vown, *yown, *acc, *gl;
   int P;
@@ -253,7 +266,7 @@ __device__ __forceinline__ void recurrence(const Rec& R, const RecLds& S, RowPtr
   while (cw < per && cw < 64) cw <<= 1;
   const int rgw = 64 / cw;
   const int rpl = (b + rgw - 1) / rgw;
-  const bool upd = per <= 64 && rpl <= kUR;
+  const bool upd = update_overlapped(b, Q, R.ld, E);
   // fold waves 1..nf; with the update overlapped, wave 3 only updates (its
   // row loads then never hold back a fold)
   const int nf = upd ? 2 : 3;
@@ -397,7 +410,9 @@ __device__ __forceinline__ void recurrence(const Rec& R, const RecLds& S, RowPtr
     } else {
       // the last wave accumulates the update of this workgroup's chunks
       // [ch0, ch1) of w: lane (rgl, cl) sums rows rgl, rgl + rgw, ... of every
-      // block for chunk ch0 + cl as soon as the block's r is in
+      // block for chunk ch0 + cl as soon as the block's r is in.  It may
+      // start work of the next step first (phase 0): its sums have slack.
+      after_folds(wave, 0);
       const int ch0 = q * per;
       const int ch1 = ch0 + per < cpr ? ch0 + per : cpr;
       const int cl = lane % cw, rgl = lane / cw;

@@ -135,6 +135,7 @@ __device__ __forceinline__ void chain_role(const TrainArgs& A, int q) {
   __shared__ int acc_ready[3];
   __shared__ int xloc;
   __shared__ int have_next;  // G_{k+1} is in the other buffer
+  __shared__ int pf_state;   // this step's early copy of G_{k+1}: 0 undecided, 1 under way, 2 not taken
   step::RecLds S{sm + L.rs, sm + L.vown, sm + L.yown, sm + L.acc, sm + L.gl, static_cast<int>(L.P),
                  &abort_flag, &r_ready, acc_ready};
   if (threadIdx.x == 0) {
@@ -196,10 +197,13 @@ __device__ __forceinline__ void chain_role(const TrainArgs& A, int q) {
       r_ready = 0;
       acc_ready[0] = acc_ready[1] = acc_ready[2] = 0;
       have_next = 0;
+      pf_state = 0;
     }
     __builtin_amdgcn_s_waitcnt(0);  // G_k (loaded now or prefetched) has landed
     __syncthreads();
-    if (threadIdx.x == 0) publish(&gfree(A)[q], tag);  // this workgroup is done with G_k's buffer
+    // this workgroup is done with G_k's buffer; published by wave 1, so the
+    // critical wave's first poll does not also wait for this store
+    if (threadIdx.x == 64) publish(&gfree(A)[q], tag);
     step::Rec R;
     R.s = s;
     R.b = b;
@@ -227,40 +231,58 @@ __device__ __forceinline__ void chain_role(const TrainArgs& A, int q) {
     // buffer, which may already hold G_{k+1}: scratch in acc when it is large
     // enough, else past both buffers
     if (A.dbl && s * NO * LW < 2048) Sk.red = S.gl + 2 * NO * S.P;
-    // wave 1 copies G_{k+1} into the other buffer, at the start of the step
-    // if the Gram has finished it by then, else after its folds; wave 2,
-    // after its folds, draws the next step's row indices and labels.  All of
-    // it has landed when the next step starts (its barrier and s_waitcnt).
+    // G_{k+1} goes into the other buffer early in the step if the Gram has
+    // finished it by then (one look), else after wave 1's folds.  A wave's
+    // LDS accesses wait for all of its direct-to-LDS copies in flight (about
+    // 8 us for these rows, which one XCD streams from memory), so the early
+    // copy goes to the wave with the most slack: the update wave when the
+    // update runs overlapped (its per-block sums catch up long before the
+    // step ends), else wave 1 (before its first fold).  Wave 2, after its
+    // folds, draws the next step's row indices and labels.  All of it has
+    // landed when the next step starts (its barrier and s_waitcnt).
+    const bool upd = step::update_overlapped(b, Q, A.ld, Elems<T>::E);
     auto prefetch = [&](int wv, int phase) {
       if (k + 1 >= A.n_outer) return;
-      if (wv == 2) {
-        if (phase == 0) return;
-        const uint64_t seed1 = splitmix64(A.base_seed, A.first + static_cast<uint64_t>(k + 1));
-        int* nidx = ibuf[(k + 1) & 1];
-        for (int p = lane; p < sb; p += 64) nidx[p] = static_cast<int>(sample(seed1, p, A.m));
-        // and the labels of the own rows (rows of the next step: own row t of
-        // minibatch j is row j*b + q + Q*t)
-        float* ny = ybuf[(k + 1) & 1];
-        for (int p = lane; p < s * NO; p += 64) {
-          const int j = p / NO, t = p - (p / NO) * NO;
-          ny[p] = t < nown ? A.y[static_cast<int>(sample(seed1, j * b + q + Q * t, A.m))] : 0.f;
-        }
-        return;
-      }
-      if (!A.dbl || s < 2 || have_next) return;
+      const bool pre = A.dbl && s >= 2;
       if (phase == 0) {
-        // one look only: folds must not wait for the Gram
+        if (!pre || wv != (upd ? 3 : 1)) return;
+        // one look only: the recurrence must not wait for the Gram
         bool ok = true;
         for (int g = lane; g < A.gram_wgs; g += 64)
           ok = ok && static_cast<int32_t>(static_cast<uint32_t>(__hip_atomic_load(
                          &gprog(A)[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) - (tag + 1)) >= 0;
-        if (!__all(ok)) return;
-      } else if (!wait_all(gprog(A), A.gram_wgs, tag + 1, A.status, A.spin, 0)) {
-        abort_flag = 1;
+        const bool go = __all(ok);
+        // the decision goes out before the copy (a later LDS store would wait for it)
+        if (lane == 0) __hip_atomic_store(&pf_state, go ? 1 : 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (!go) return;
+        step::load_g_rows<16>(A.G[(k + 1) % kRing], gbuf[(k + 1) & 1], s, b, Q, q, nown, S.P, wv, 1);
+        if (lane == 0) have_next = 1;
         return;
       }
-      step::load_g_rows<16>(A.G[(k + 1) % kRing], gbuf[(k + 1) & 1], s, b, Q, q, nown, S.P, 1, 1);
-      if (lane == 0) have_next = 1;
+      if (wv == 1) {
+        // the copy the early look did not take
+        if (!pre || !step::lds_wait(&pf_state, 1, &abort_flag, A.status, A.spin) ||
+            __hip_atomic_load(&pf_state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 1)
+          return;
+        if (!wait_all(gprog(A), A.gram_wgs, tag + 1, A.status, A.spin, 0)) {
+          abort_flag = 1;
+          return;
+        }
+        step::load_g_rows<16>(A.G[(k + 1) % kRing], gbuf[(k + 1) & 1], s, b, Q, q, nown, S.P, 1, 1);
+        if (lane == 0) have_next = 1;
+        return;
+      }
+      // wave 2
+      const uint64_t seed1 = splitmix64(A.base_seed, A.first + static_cast<uint64_t>(k + 1));
+      int* nidx = ibuf[(k + 1) & 1];
+      for (int p = lane; p < sb; p += 64) nidx[p] = static_cast<int>(sample(seed1, p, A.m));
+      // and the labels of the own rows (rows of the next step: own row t of
+      // minibatch j is row j*b + q + Q*t)
+      float* ny = ybuf[(k + 1) & 1];
+      for (int p = lane; p < s * NO; p += 64) {
+        const int j = p / NO, t = p - (p / NO) * NO;
+        ny[p] = t < nown ? A.y[static_cast<int>(sample(seed1, j * b + q + Q * t, A.m))] : 0.f;
+      }
     };
     step::recurrence<T, NO, CP>(R, Sk, [&](int row) { return X4 + static_cast<int64_t>(idx[row]) * cpr; },
                                 prefetch);
