@@ -46,6 +46,7 @@ def _data(loss, m, n, seed):
     (3000, 28, 32, 128, 2),   # HIGGS-like: G rows too large for LDS, 2 rows per workgroup
     (4000, 512, 8, 256, 2),   # synth-like: 4 rows per workgroup, 4 columns per lane
     (2000, 64, 40, 64, 2),    # one row per workgroup with G too large for LDS
+    (4000, 3000, 4, 64, 3),   # update after the recurrence in the persistent launch (16 rows per lane)
 ])
 def test_train_equals_outer_steps(form, loss, m, n, s, b, n_outer):
     import torch
