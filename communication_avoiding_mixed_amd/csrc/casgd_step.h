@@ -236,6 +236,10 @@ __device__ __forceinline__ void update_after(const Rec& R, const float* rs, floa
 // 256 lanes.  rowp(row) points at the 16-byte chunks of row `row` (0 <=
 // row < s*b) of the step's Y.  Ends with the new weights of the workgroup's
 // columns written (and every wave past its last LDS access).
+// after_folds(wave, phase) lets a caller run other work on the waves with
+// slack: phase 0 on waves 1 and 2 before their first fold and on the update
+// wave (when the update is overlapped) before its first block, phase 1 on
+// waves 1 and 2 after their last fold.
 struct NoHook {
   __device__ void operator()(int, int) const {}
 };
