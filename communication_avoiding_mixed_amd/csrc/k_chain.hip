@@ -307,6 +307,57 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
     // r of block tb is in, it folds G_{k,tb} r_tb into their partial sums
     // for every k >= tb + 2, two blocks at a time with all loads issued first
     const int h = wv - 1;
+    // G in global memory (rows too large for LDS): up to NBW blocks' loads
+    // are all issued (clamped, unconditional) before any is used, so a fold
+    // step waits about one memory latency per batch, not one per pair.  Past
+    // the last block the clamped loads are wasted, so the batch is kept
+    // short: on MI355X at b = 128, s = 32 batches of 3 / 4 / 6 / 8 / 12 / 16
+    // blocks gave 101 / 97.6 / 97.3 / 97.6 / 103.7 / 116 us per outer step.
+    // The loads do not depend on r, so the first batch of fold(tb) is issued
+    // before the wait for r of block tb (g0) and its latency overlaps it.
+    constexpr int NBW = NO * CP <= 4 ? 6 : 3;
+    const bool glob = PRE == 0 || (PRE == 2 && !a.preload);
+    float g0[NBW][NO][CP];
+    auto first_k = [&](int tb) {
+      int k0 = tb + 2;
+      return k0 + (h - k0 % nf + nf) % nf;  // first k >= tb+2 with k = h (mod nf)
+    };
+    auto load_batch = [&](int tb, int k, float (&gb)[NBW][NO][CP]) {
+#pragma unroll
+      for (int e = 0; e < NBW; ++e) {
+        const int kk = k + e * nf;
+        const int kc = kk < s ? kk : s - 1;
+#pragma unroll
+        for (int t = 0; t < NO; ++t)
+#pragma unroll
+          for (int u = 0; u < CP; ++u) {
+            const int l = lane + 64 * u;
+            gb[e][t][u] = gval(kc, t < nown ? t : 0, tb * b + (l < b ? l : 0));
+          }
+      }
+    };
+    auto use_batch = [&](int k, const float (&gb)[NBW][NO][CP], const float (&rr)[CP]) {
+#pragma unroll
+      for (int e = 0; e < NBW; ++e) {
+        const int kk = k + e * nf;
+#pragma unroll
+        for (int t = 0; t < NO; ++t)
+#pragma unroll
+          for (int u = 0; u < CP; ++u) {
+            const int l = lane + 64 * u;
+            if (kk < s && t < nown && l < b) {
+              float* ap = &acc[(kk * nown_max + t) * LWc + l];
+              *ap = fmaf(gb[e][t][u], rr[u], *ap);
+            }
+          }
+      }
+    };
+    // before the wait for r of block tb: the first batch of fold(tb)
+    auto pre_load = [&](int tb) {
+      if (glob && tb + 2 < s) load_batch(tb, first_k(tb), g0);
+    };
+    // after r of block tb is in: fold G_{k,tb} r_tb into the partial sums of
+    // this wave's blocks k >= tb + 2 (pre_load(tb) ran first)
     auto fold = [&](int tb) {
       float rr[CP];
 #pragma unroll
@@ -314,45 +365,17 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
         const int l = lane + 64 * u;
         rr[u] = (l < b) ? rs[tb * b + l] : 0.f;
       }
-      int k0 = tb + 2;
-      k0 += (h - k0 % nf + nf) % nf;  // first k >= tb+2 with k = h (mod nf)
-      if (PRE == 0 || (PRE == 2 && !a.preload)) {
-        // G in global memory (rows too large for LDS): up to NBW blocks'
-        // loads are all issued (clamped, unconditional) before any is used,
-        // so a fold step waits about one memory latency per batch, not one
-        // per pair.  Past the last block the clamped loads are wasted, so
-        // the batch is kept short: on MI355X at b = 128, s = 32 batches of
-        // 3 / 4 / 6 / 8 / 12 / 16 blocks gave 101 / 97.6 / 97.3 / 97.6 /
-        // 103.7 / 116 us per outer step.
-        constexpr int NBW = NO * CP <= 4 ? 6 : 3;
-        for (int k = k0; k < s; k += NBW * nf) {
+      const int k0 = first_k(tb);
+      if (glob) {
+        int k = k0;
+        if (k < s) {
+          use_batch(k, g0, rr);
+          k += NBW * nf;
+        }
+        for (; k < s; k += NBW * nf) {
           float gb[NBW][NO][CP];
-#pragma unroll
-          for (int e = 0; e < NBW; ++e) {
-            const int kk = k + e * nf;
-            const int kc = kk < s ? kk : s - 1;
-#pragma unroll
-            for (int t = 0; t < NO; ++t)
-#pragma unroll
-              for (int u = 0; u < CP; ++u) {
-                const int l = lane + 64 * u;
-                gb[e][t][u] = gval(kc, t < nown ? t : 0, tb * b + (l < b ? l : 0));
-              }
-          }
-#pragma unroll
-          for (int e = 0; e < NBW; ++e) {
-            const int kk = k + e * nf;
-#pragma unroll
-            for (int t = 0; t < NO; ++t)
-#pragma unroll
-              for (int u = 0; u < CP; ++u) {
-                const int l = lane + 64 * u;
-                if (kk < s && t < nown && l < b) {
-                  float* ap = &acc[(kk * nown_max + t) * LWc + l];
-                  *ap = fmaf(gb[e][t][u], rr[u], *ap);
-                }
-              }
-          }
+          load_batch(tb, k, gb);
+          use_batch(k, gb, rr);
         }
         lds_publish(&acc_ready[h], tb + 1);
         return;
@@ -389,6 +412,7 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
     };
     if (!(upd && wv == kWaves - 1)) {
       for (int tb = 0; tb + 2 < s; ++tb) {
+        pre_load(tb);
         if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status, a.spin)) break;
         fold(tb);
       }
@@ -416,6 +440,7 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
         }
       };
       auto step = [&](int tb, const u32x4 (&src)[kUpdRows]) -> bool {
+        pre_load(tb);
         if (!lds_wait(&r_ready, tb + 1, &abort_flag, a.status, a.spin)) return false;
         if (tb + 2 < s) fold(tb);
 #pragma unroll
