@@ -313,11 +313,13 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
     // the last block the clamped loads are wasted, so the batch is kept
     // short: on MI355X at b = 128, s = 32 batches of 3 / 4 / 6 / 8 / 12 / 16
     // blocks gave 101 / 97.6 / 97.3 / 97.6 / 103.7 / 116 us per outer step.
-    // The loads do not depend on r, so the first batch of fold(tb) is issued
-    // before the wait for r of block tb (g0) and its latency overlaps it.
+    // The loads do not depend on r, so the first batch of fold(tb), and the
+    // second when the fold has one, are issued before the wait for r of block
+    // tb (g0, g1) and their latency overlaps it.
     constexpr int NBW = NO * CP <= 4 ? 6 : 3;
     const bool glob = PRE == 0 || (PRE == 2 && !a.preload);
-    float g0[NBW][NO][CP];
+    float g0[NBW][NO][CP], g1[NBW][NO][CP];
+    bool two = false;  // g1 holds the second batch of the coming fold
     auto first_k = [&](int tb) {
       int k0 = tb + 2;
       return k0 + (h - k0 % nf + nf) % nf;  // first k >= tb+2 with k = h (mod nf)
@@ -352,9 +354,15 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
           }
       }
     };
-    // before the wait for r of block tb: the first batch of fold(tb)
+    // before the wait for r of block tb: the first one or two batches of
+    // fold(tb)
     auto pre_load = [&](int tb) {
-      if (glob && tb + 2 < s) load_batch(tb, first_k(tb), g0);
+      if (glob && tb + 2 < s) {
+        const int k0 = first_k(tb);
+        load_batch(tb, k0, g0);
+        two = k0 + NBW * nf < s;
+        if (two) load_batch(tb, k0 + NBW * nf, g1);
+      }
     };
     // after r of block tb is in: fold G_{k,tb} r_tb into the partial sums of
     // this wave's blocks k >= tb + 2 (pre_load(tb) ran first)
@@ -370,6 +378,10 @@ __device__ __forceinline__ bool recurrence_fast(const FastCtx& x) {
         int k = k0;
         if (k < s) {
           use_batch(k, g0, rr);
+          k += NBW * nf;
+        }
+        if (two) {
+          use_batch(k, g1, rr);
           k += NBW * nf;
         }
         for (; k < s; k += NBW * nf) {
